@@ -1,0 +1,162 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) single-token routed-expert MoE
+ * decode layer.
+ *
+ * The layer, for each of M tokens x[m, :] (hidden size H):
+ *   1. router GEMV     logits[m, e] = sum_h Wr[e, h] x[m, h]                  (E experts)
+ *   2. top-K + softmax expert_ids[m, :] = the K largest logits, largest first,
+ *                      equal logits -> lower expert id first;
+ *                      weights = softmax over all E taken at those ids, divided
+ *                      by their sum when renormalize != 0
+ *   3. W13 GEMV + SiLU activated[m, k, j] = silu(g) * u with
+ *                      g = sum_h W13[e, j, h] x[m, h], u = sum_h W13[e, I + j, h] x[m, h],
+ *                      e = expert_ids[m, k], silu(g) = g / (1 + exp(-g))
+ *   4. W2 GEMV + combine r[m, h] = sum_k weights[m, k] sum_j W2[e, h, j] activated[m, k, j]
+ *   5. shared expert   s[m, h] = the same gate/up -> SiLU*mul -> down chain with
+ *                      the shared expert's weights, added with weight 1:
+ *                      y[m, h] = fp16(r[m, h] + s[m, h])   (one rounding)
+ *
+ * Where the pages define it:
+ *   "如何在天垓 BI-V100 上优化大模型推理：一份工作日志" (BI-V100 inference
+ *   worklog): part 3 -- the MoE fallback gathers the selected experts' weights
+ *   with index_select and re-reads them; the direct_routed method indexes the
+ *   expert tensor by expert id inside the GEMV instead (steps 3 and 4);
+ *   part 10 -- the W13 kernel maps input(1, H) x W13[expert_ids[k], row, :] to
+ *   gate_up(K, 2I); the W2 kernel maps activated(K, I) x W2[expert_ids[k], h, :]
+ *   to expert_out(H) with the weighted sum; part 8 -- the routing step is a
+ *   top-k and a softmax; part 2 -- the shared expert is gate_up, SiluAndMul and
+ *   down.  "decode analysis report 2026-07-14", profiling section: the MoE
+ *   block is gate, routing top-k, routed experts and shared expert.
+ *
+ * Conventions for every entry point:
+ *   - fp16 tensors are IEEE binary16, row-major, contiguous, passed as void*.
+ *   - All tensor pointers are DEVICE pointers of the current HIP device; the
+ *     caller owns every buffer (including the workspace) and keeps it alive
+ *     until the work queued on `stream` has finished.  The library keeps no
+ *     pointer after a call returns and holds no mutable global state.
+ *   - Every call only enqueues kernels on `stream`: it never allocates, never
+ *     synchronises and never reads device memory on the host, so it may be
+ *     recorded into a hipGraph by stream capture.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and a negative moe_status is returned.
+ *   - Device-data preconditions are NOT checked (no device reads on the host):
+ *     expert ids must lie in [0, E) and be distinct within a token; all values
+ *     must be finite.  Violating them is undefined behaviour.
+ *   - M = 0 is a valid empty call: nothing is enqueued, MOE_OK is returned.
+ *
+ * Supported sizes (MOE_ERR_SHAPE otherwise):
+ *   0 <= M <= 8;  H in {512, 1024, 2048, 4096} (H = 4096 needs M <= 4);
+ *   1 <= E <= 1024;  1 <= K <= min(E, 16);
+ *   I and Is in {64, 128, 256, 512, 1024, 2048}.
+ * Alignment (MOE_ERR_ALIGN otherwise): fp16 tensors 16 bytes, fp32/int32
+ * arrays 4 bytes, workspace 256 bytes.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+#define MOE_MAX_TOKENS 8
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_EXPERTS 1024
+
+typedef int moe_status;
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)        /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)       /* a size is outside the supported set */
+#define MOE_ERR_ALIGN (-3)       /* a pointer is not aligned as required */
+#define MOE_ERR_WORKSPACE (-4)   /* ws_bytes < moe_workspace_bytes(...) */
+#define MOE_ERR_HIP (-5)         /* a kernel launch failed (hipGetLastError) */
+
+/* ABI version of the loaded library (MOE_ABI_VERSION it was built with). */
+int moe_abi_version(void);
+
+/* Static English description of a status code; never NULL. */
+const char *moe_status_str(moe_status status);
+
+/* Bytes of device workspace `ws` that shared_expert and moe_decode_fused need
+ * for these sizes (one buffer of this size serves both calls when they are
+ * issued on the same stream).  Returns 0 for unsupported sizes. */
+size_t moe_workspace_bytes(int M, int H, int E, int I, int K, int Is);
+
+/* Steps 1-2: router GEMV, top-K selection and routing weights.
+ *   x           [M, H]  fp16   token activations
+ *   w_router    [E, H]  fp16   router weight
+ *   renormalize 0: weights are the full softmax at the selected ids;
+ *               else: divided by their sum (the weights then sum to 1)
+ *   topk_ids    [M, K]  int32  out: selected expert ids, largest logit first,
+ *                              equal logits -> lower id first
+ *   topk_w      [M, K]  fp32   out: routing weights in the same order
+ *   logits      [M, E]  fp32   out: router logits (needed by the selection;
+ *                              also returned for diagnostics)
+ * Arithmetic: fp16 products accumulated in fp32; softmax in fp32. */
+moe_status moe_route(const void *x, const void *w_router, int M, int H, int E, int K,
+                     int renormalize, int32_t *topk_ids, float *topk_w, float *logits,
+                     hipStream_t stream);
+
+/* Step 5 on its own: the shared expert (no routing, weight 1).
+ *   x          [M, H]    fp16
+ *   w_gate_up  [2Is, H]  fp16  rows [0, Is) gate, rows [Is, 2Is) up
+ *   w_down     [H, Is]   fp16
+ *   s_out      [M, H]    fp32  out: shared-expert output, not rounded to fp16
+ *   ws         device workspace of at least moe_workspace_bytes(M, H, 1, 64, 1, Is)
+ *              bytes (any of the call's sizes work; only Is matters here)
+ * Arithmetic: fp32 accumulation; the SiLU*mul activation is kept in fp32. */
+moe_status shared_expert(const void *x, const void *w_gate_up, const void *w_down, int M, int H,
+                         int Is, float *s_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Steps 3-5 fused: expert-indexed W13 GEMV with SiLU*mul in its epilogue, then
+ * the W2 GEMV with the weighted combine, the optional shared-expert add and
+ * the single fp16 rounding.  The expert tensors are read in place at
+ * W13 + expert_id * (2I*H) and W2 + expert_id * (H*I): no gathered copy.
+ * With M > 1 every distinct selected expert's rows are read once for all the
+ * tokens that route to it.
+ *   x          [M, H]      fp16
+ *   w13        [E, 2I, H]  fp16  per expert: rows [0, I) gate, rows [I, 2I) up
+ *   w2         [E, H, I]   fp16
+ *   topk_ids   [M, K]      int32 (from moe_route or the caller)
+ *   topk_w     [M, K]      fp32
+ *   shared_in  [M, H]      fp32 or NULL: added to the routed sum before rounding
+ *   y          [M, H]      fp16  out
+ *   ws         device workspace, >= moe_workspace_bytes(M, H, E, I, K, 0) bytes
+ * Summation order is fixed (no atomics): per token, experts in routing order
+ * (for M > 1: in order of first appearance scanning topk_ids row by row), the
+ * shared term last; results are bitwise reproducible run to run. */
+moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
+                            const int32_t *topk_ids, const float *topk_w, const float *shared_in,
+                            int M, int H, int E, int I, int K, void *y, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* ---- test-only probes (not part of the decode path) --------------------- */
+
+/* Sums 64 fp32 values with one wavefront's cross-lane (DPP) reduction, the
+ * same routine the GEMV kernels use; out[0] = the sum.  in: [64] device. */
+moe_status moe_dbg_wave_sum(const float *in, float *out, hipStream_t stream);
+
+/* Step 3 alone: activated [M, K, I] fp32 written to `activated` (device, may be
+ * the caller's buffer); same arguments as moe_decode_fused otherwise. */
+moe_status moe_dbg_w13_silu(const void *x, const void *w13, const int32_t *topk_ids, int M, int H,
+                            int E, int I, int K, float *activated, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Step 4 alone, with injected activations: the W2 GEMV + weighted combine (+
+ * shared_in) of moe_decode_fused reading `activated` [M, K, I] fp32 (device)
+ * instead of the W13 stage's output; same arguments as moe_decode_fused
+ * otherwise. */
+moe_status moe_dbg_w2_combine(const float *activated, const void *w2, const int32_t *topk_ids,
+                              const float *topk_w, const float *shared_in, int M, int H, int E,
+                              int I, int K, void *y, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

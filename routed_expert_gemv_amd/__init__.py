@@ -1,5 +1,12 @@
 """MI355X-native single-token routed-expert MoE decode layer (HIP, gfx950).
 
 The compute path is the C-ABI library ``libmoe_decode.so`` built from
-``csrc/``; the Python functions exported here only marshal tensors into it.
+``csrc/`` (declared in ``include/moe_decode.h``); the functions exported here
+only marshal torch tensors into it.  Importing the package does not load the
+library; the first call does, and raises if it is missing and cannot be built.
 """
+from .api import (MoeError, moe_abi_version, moe_dbg_w13_silu, moe_dbg_w2_combine, moe_dbg_wave_sum,
+                  moe_decode_fused, moe_route, moe_workspace_bytes, shared_expert, workspace)
+
+__all__ = ["MoeError", "moe_abi_version", "moe_dbg_w13_silu", "moe_dbg_w2_combine", "moe_dbg_wave_sum",
+           "moe_decode_fused", "moe_route", "moe_workspace_bytes", "shared_expert", "workspace"]

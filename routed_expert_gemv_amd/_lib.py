@@ -1,0 +1,59 @@
+"""ctypes loader of libmoe_decode.so and the prototypes of include/moe_decode.h."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+from . import build as _build
+
+_lock = threading.Lock()
+_lib = None
+
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
+                -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
+EXPORTED = ["moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
+            "shared_expert", "moe_decode_fused", "moe_dbg_wave_sum", "moe_dbg_w13_silu",
+            "moe_dbg_w2_combine"]
+
+_vp = C.c_void_p
+_i = C.c_int
+_sz = C.c_size_t
+
+
+def lib() -> C.CDLL:
+    """The loaded library; built in-tree first if it is missing.  Raises if it
+    cannot be built or loaded: there is no other implementation to fall back to."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_build.LIB):  # load what is built; build only if nothing is
+                _build.build(force=True)
+            L = C.CDLL(_build.LIB)
+            L.moe_abi_version.restype = _i
+            L.moe_abi_version.argtypes = []
+            L.moe_status_str.restype = C.c_char_p
+            L.moe_status_str.argtypes = [_i]
+            L.moe_workspace_bytes.restype = _sz
+            L.moe_workspace_bytes.argtypes = [_i] * 6
+            L.moe_route.restype = _i
+            L.moe_route.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp]
+            L.shared_expert.restype = _i
+            L.shared_expert.argtypes = [_vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]
+            L.moe_decode_fused.restype = _i
+            L.moe_decode_fused.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                           _vp, _vp, _sz, _vp]
+            L.moe_dbg_wave_sum.restype = _i
+            L.moe_dbg_wave_sum.argtypes = [_vp, _vp, _vp]
+            L.moe_dbg_w13_silu.restype = _i
+            L.moe_dbg_w13_silu.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]
+            L.moe_dbg_w2_combine.restype = _i
+            L.moe_dbg_w2_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
+                                             _vp, _sz, _vp]
+            _lib = L
+    return _lib
+
+
+def path() -> str:
+    return _build.LIB

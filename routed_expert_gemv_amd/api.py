@@ -1,0 +1,204 @@
+"""Python binding of the C ABI in include/moe_decode.h (same names).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe_decode.so.  Tensors are torch tensors on the current HIP device; torch
+provides device memory and streams, nothing else.  A non-zero status from the
+library raises MoeError.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.lib().moe_status_str(int(status)).decode()
+        super().__init__("%s: %s (%s)" % (fn, msg, _lib.STATUS_NAMES.get(status, status)))
+        self.status = status
+
+
+def _check(fn, st):
+    if st != 0:
+        raise MoeError(fn, st)
+
+
+def _dev_tensor(name, t, dtype, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor, got %s" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    return t
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def moe_abi_version() -> int:
+    return int(_lib.lib().moe_abi_version())
+
+
+def moe_workspace_bytes(M: int, H: int, E: int, I: int, K: int, Is: int = 0) -> int:
+    return int(_lib.lib().moe_workspace_bytes(M, H, E, I, K, Is))
+
+
+def workspace(M: int, H: int, E: int, I: int, K: int, Is: int = 0, device=None) -> torch.Tensor:
+    """A device workspace big enough for shared_expert and moe_decode_fused."""
+    n = moe_workspace_bytes(M, H, E, I, K, Is)
+    if n == 0:
+        raise MoeError("moe_workspace_bytes", -2)
+    return torch.empty(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
+
+
+def moe_route(x, w_router, K: int, renormalize: bool = True, topk_ids=None, topk_w=None,
+              logits=None, stream=None):
+    """Router GEMV + top-K + routing weights.  Returns (topk_ids, topk_w, logits)."""
+    _dev_tensor("x", x, torch.float16, 2)
+    _dev_tensor("w_router", w_router, torch.float16, 2)
+    M, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("w_router must be [E, %d], got %s" % (H, tuple(w_router.shape)))
+    dev = x.device
+    topk_ids = torch.empty((M, K), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
+    topk_w = torch.empty((M, K), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    logits = torch.empty((M, E), dtype=torch.float32, device=dev) if logits is None else logits
+    _dev_tensor("topk_ids", topk_ids, torch.int32)
+    _dev_tensor("topk_w", topk_w, torch.float32)
+    _dev_tensor("logits", logits, torch.float32)
+    if topk_ids.numel() != M * K or topk_w.numel() != M * K or logits.numel() != M * E:
+        raise ValueError("output sizes do not match M=%d K=%d E=%d" % (M, K, E))
+    st = _lib.lib().moe_route(_ptr(x), _ptr(w_router), M, H, E, K, int(bool(renormalize)),
+                              _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _stream(stream, dev))
+    _check("moe_route", st)
+    return topk_ids, topk_w, logits
+
+
+def shared_expert(x, w_gate_up, w_down, s_out=None, ws=None, stream=None):
+    """Shared expert (gate_up -> SiLU*mul -> down) into fp32 s_out [M, H]."""
+    _dev_tensor("x", x, torch.float16, 2)
+    _dev_tensor("w_gate_up", w_gate_up, torch.float16, 2)
+    _dev_tensor("w_down", w_down, torch.float16, 2)
+    M, H = x.shape
+    Is = w_gate_up.shape[0] // 2
+    if w_gate_up.shape != (2 * Is, H) or w_down.shape != (H, Is):
+        raise ValueError("shared expert shapes: gate_up %s, down %s for H=%d"
+                         % (tuple(w_gate_up.shape), tuple(w_down.shape), H))
+    dev = x.device
+    s_out = torch.empty((M, H), dtype=torch.float32, device=dev) if s_out is None else s_out
+    _dev_tensor("s_out", s_out, torch.float32)
+    if s_out.numel() != M * H:
+        raise ValueError("s_out must have M*H elements")
+    if ws is None:
+        ws = torch.empty(max(M, 1) * Is * 4, dtype=torch.uint8, device=dev)
+    _dev_tensor("ws", ws, torch.uint8)
+    st = _lib.lib().shared_expert(_ptr(x), _ptr(w_gate_up), _ptr(w_down), M, H, Is, _ptr(s_out),
+                                  _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check("shared_expert", st)
+    return s_out
+
+
+def moe_decode_fused(x, w13, w2, topk_ids, topk_w, shared_in=None, y=None, ws=None, stream=None):
+    """Expert-indexed W13 + SiLU*mul, W2 + weighted combine (+ shared_in) -> fp16 y [M, H]."""
+    _dev_tensor("x", x, torch.float16, 2)
+    _dev_tensor("w13", w13, torch.float16, 3)
+    _dev_tensor("w2", w2, torch.float16, 3)
+    _dev_tensor("topk_ids", topk_ids, torch.int32)
+    _dev_tensor("topk_w", topk_w, torch.float32)
+    M, H = x.shape
+    E, twoI, H2 = w13.shape
+    I = twoI // 2
+    K = topk_ids.shape[-1]
+    if H2 != H or w2.shape != (E, H, I):
+        raise ValueError("expert shapes: w13 %s, w2 %s for H=%d"
+                         % (tuple(w13.shape), tuple(w2.shape), H))
+    if topk_ids.numel() != M * K or topk_w.numel() != M * K:
+        raise ValueError("topk_ids / topk_w must be [M, K]")
+    dev = x.device
+    if shared_in is not None:
+        _dev_tensor("shared_in", shared_in, torch.float32)
+        if shared_in.numel() != M * H:
+            raise ValueError("shared_in must be [M, H]")
+    y = torch.empty((M, H), dtype=torch.float16, device=dev) if y is None else y
+    _dev_tensor("y", y, torch.float16)
+    if y.numel() != M * H:
+        raise ValueError("y must be [M, H]")
+    if ws is None:
+        ws = workspace(max(M, 1), H, E, I, K, 0, dev)
+    _dev_tensor("ws", ws, torch.uint8)
+    st = _lib.lib().moe_decode_fused(_ptr(x), _ptr(w13), _ptr(w2), _ptr(topk_ids), _ptr(topk_w),
+                                     _ptr(shared_in), M, H, E, I, K, _ptr(y), _ptr(ws), ws.numel(),
+                                     _stream(stream, dev))
+    _check("moe_decode_fused", st)
+    return y
+
+
+def moe_dbg_wave_sum(values, out=None, stream=None):
+    """Test probe: the 64 fp32 values summed by one wave's cross-lane reduction."""
+    _dev_tensor("values", values, torch.float32)
+    if values.numel() != 64:
+        raise ValueError("values must hold 64 elements")
+    out = torch.empty(1, dtype=torch.float32, device=values.device) if out is None else out
+    st = _lib.lib().moe_dbg_wave_sum(_ptr(values), _ptr(out), _stream(stream, values.device))
+    _check("moe_dbg_wave_sum", st)
+    return out
+
+
+def moe_dbg_w13_silu(x, w13, topk_ids, activated=None, ws=None, stream=None):
+    """Test probe: the W13 + SiLU*mul stage alone -> activated [M, K, I] fp32."""
+    _dev_tensor("x", x, torch.float16, 2)
+    _dev_tensor("w13", w13, torch.float16, 3)
+    _dev_tensor("topk_ids", topk_ids, torch.int32)
+    M, H = x.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    K = topk_ids.shape[-1]
+    dev = x.device
+    activated = (torch.zeros((M, K, I), dtype=torch.float32, device=dev)
+                 if activated is None else activated)
+    _dev_tensor("activated", activated, torch.float32)
+    if ws is None:
+        ws = workspace(max(M, 1), H, E, I, K, 0, dev)
+    st = _lib.lib().moe_dbg_w13_silu(_ptr(x), _ptr(w13), _ptr(topk_ids), M, H, E, I, K,
+                                     _ptr(activated), _ptr(ws), ws.numel(), _stream(stream, dev))
+    _check("moe_dbg_w13_silu", st)
+    return activated
+
+
+def moe_dbg_w2_combine(activated, w2, topk_ids, topk_w, shared_in=None, y=None, ws=None,
+                       stream=None):
+    """Test probe: the W2 + combine stage alone on injected activations [M, K, I] fp32."""
+    _dev_tensor("activated", activated, torch.float32, 3)
+    _dev_tensor("w2", w2, torch.float16, 3)
+    _dev_tensor("topk_ids", topk_ids, torch.int32)
+    _dev_tensor("topk_w", topk_w, torch.float32)
+    M, K, I = activated.shape
+    E, H, I2 = w2.shape
+    if I2 != I or topk_ids.numel() != M * K or topk_w.numel() != M * K:
+        raise ValueError("shapes do not match activated [M, K, I]")
+    dev = activated.device
+    if shared_in is not None:
+        _dev_tensor("shared_in", shared_in, torch.float32)
+    y = torch.empty((M, H), dtype=torch.float16, device=dev) if y is None else y
+    _dev_tensor("y", y, torch.float16)
+    if ws is None:
+        ws = workspace(max(M, 1), H, E, I, K, 0, dev)
+    st = _lib.lib().moe_dbg_w2_combine(_ptr(activated), _ptr(w2), _ptr(topk_ids), _ptr(topk_w),
+                                       _ptr(shared_in), M, H, E, I, K, _ptr(y), _ptr(ws),
+                                       ws.numel(), _stream(stream, dev))
+    _check("moe_dbg_w2_combine", st)
+    return y

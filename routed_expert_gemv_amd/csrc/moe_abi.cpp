@@ -1,0 +1,137 @@
+// moe_abi.cpp -- C ABI entry points of libmoe_decode (declared in
+// include/moe_decode.h): host-side argument validation, workspace carving and
+// kernel launches on the caller's stream.  Every check runs before anything is
+// enqueued; nothing here allocates, synchronises or reads device memory.
+#include "moe_decode.h"
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool h_ok(int H) { return H == 512 || H == 1024 || H == 2048 || H == 4096; }
+bool i_ok(int I) { return I == 64 || I == 128 || I == 256 || I == 512 || I == 1024 || I == 2048; }
+bool m_ok(int M, int H) { return M >= 0 && M <= kMaxTokens && (H < 4096 || M <= 4); }
+bool ek_ok(int E, int K) { return E >= 1 && E <= kMaxExperts && K >= 1 && K <= kMaxTopk && K <= E; }
+
+bool al(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t routed_ws_bytes(int M, int I, int K)
+{
+    return kRoutedActOffset + align256((size_t)M * K * I * sizeof(float));
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+} // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_str(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is outside the supported set";
+    case MOE_ERR_ALIGN: return "a pointer is not aligned as required";
+    case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP: return "a kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+size_t moe_workspace_bytes(int M, int H, int E, int I, int K, int Is)
+{
+    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (Is != 0 && !i_ok(Is))) return 0;
+    return routed_ws_bytes(M < 1 ? 1 : M, I, K);
+}
+
+moe_status moe_route(const void *x, const void *w_router, int M, int H, int E, int K,
+                     int renormalize, int32_t *topk_ids, float *topk_w, float *logits,
+                     hipStream_t stream)
+{
+    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K)) return MOE_ERR_SHAPE;
+    if (M == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_w || !logits) return MOE_ERR_NULL;
+    if (!al(x, 16) || !al(w_router, 16) || !al(topk_ids, 4) || !al(topk_w, 4) || !al(logits, 4))
+        return MOE_ERR_ALIGN;
+    return hip_status(launch_route(x, w_router, M, H, E, K, renormalize, topk_ids, topk_w, logits,
+                                   stream));
+}
+
+moe_status shared_expert(const void *x, const void *w_gate_up, const void *w_down, int M, int H,
+                         int Is, float *s_out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!m_ok(M, H) || !h_ok(H) || !i_ok(Is)) return MOE_ERR_SHAPE;
+    if (M == 0) return MOE_OK;
+    if (!x || !w_gate_up || !w_down || !s_out || !ws) return MOE_ERR_NULL;
+    if (!al(x, 16) || !al(w_gate_up, 16) || !al(w_down, 16) || !al(s_out, 4) || !al(ws, 256))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < (size_t)M * Is * sizeof(float)) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_shared(x, w_gate_up, w_down, M, H, Is, s_out,
+                                    static_cast<float *>(ws), stream));
+}
+
+moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
+                            const int32_t *topk_ids, const float *topk_w, const float *shared_in,
+                            int M, int H, int E, int I, int K, void *y, void *ws, size_t ws_bytes,
+                            hipStream_t stream)
+{
+    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I)) return MOE_ERR_SHAPE;
+    if (M == 0) return MOE_OK;
+    if (!x || !w13 || !w2 || !topk_ids || !topk_w || !y || !ws) return MOE_ERR_NULL;
+    if (!al(x, 16) || !al(w13, 16) || !al(w2, 16) || !al(topk_ids, 4) || !al(topk_w, 4) ||
+        !al(y, 2) || !al(ws, 256) || (shared_in && !al(shared_in, 4)))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < routed_ws_bytes(M, I, K)) return MOE_ERR_WORKSPACE;
+    char *base = static_cast<char *>(ws);
+    return hip_status(launch_fused(x, w13, w2, topk_ids, topk_w, shared_in, M, H, E, I, K, y,
+                                   reinterpret_cast<float *>(base + kRoutedActOffset),
+                                   reinterpret_cast<GroupTable *>(base + kGroupOffset), stream));
+}
+
+moe_status moe_dbg_wave_sum(const float *in, float *out, hipStream_t stream)
+{
+    if (!in || !out) return MOE_ERR_NULL;
+    if (!al(in, 4) || !al(out, 4)) return MOE_ERR_ALIGN;
+    return hip_status(launch_dbg_wave_sum(in, out, stream));
+}
+
+moe_status moe_dbg_w13_silu(const void *x, const void *w13, const int32_t *topk_ids, int M, int H,
+                            int E, int I, int K, float *activated, void *ws, size_t ws_bytes,
+                            hipStream_t stream)
+{
+    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I)) return MOE_ERR_SHAPE;
+    if (M == 0) return MOE_OK;
+    if (!x || !w13 || !topk_ids || !activated || !ws) return MOE_ERR_NULL;
+    if (!al(x, 16) || !al(w13, 16) || !al(topk_ids, 4) || !al(activated, 16) || !al(ws, 256))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < routed_ws_bytes(M, I, K)) return MOE_ERR_WORKSPACE;
+    char *base = static_cast<char *>(ws);
+    return hip_status(launch_w13_routed(x, w13, topk_ids, M, H, E, I, K, activated,
+                                        reinterpret_cast<GroupTable *>(base + kGroupOffset),
+                                        stream));
+}
+
+moe_status moe_dbg_w2_combine(const float *activated, const void *w2, const int32_t *topk_ids,
+                              const float *topk_w, const float *shared_in, int M, int H, int E,
+                              int I, int K, void *y, void *ws, size_t ws_bytes,
+                              hipStream_t stream)
+{
+    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I)) return MOE_ERR_SHAPE;
+    if (M == 0) return MOE_OK;
+    if (!activated || !w2 || !topk_ids || !topk_w || !y || !ws) return MOE_ERR_NULL;
+    if (!al(activated, 16) || !al(w2, 16) || !al(topk_ids, 4) || !al(topk_w, 4) || !al(y, 2) ||
+        !al(ws, 256) || (shared_in && !al(shared_in, 4)))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < routed_ws_bytes(M, I, K)) return MOE_ERR_WORKSPACE;
+    char *base = static_cast<char *>(ws);
+    return hip_status(launch_w2_routed(activated, w2, topk_ids, topk_w, shared_in, M, H, E, I, K,
+                                       y, reinterpret_cast<GroupTable *>(base + kGroupOffset),
+                                       stream));
+}
+
+} // extern "C"

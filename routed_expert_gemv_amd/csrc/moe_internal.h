@@ -1,0 +1,55 @@
+// moe_internal.h -- shared between the kernels (moe_kernels.hip) and the host
+// entry points (moe_abi.cpp); not part of the public ABI.
+#ifndef MOE_INTERNAL_H
+#define MOE_INTERNAL_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxTokens = 8;
+constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxSlots = kMaxTokens * kMaxTopk; // M*K entries of topk_ids
+constexpr int kMaxInter = 2048;                  // largest I / Is
+
+// Distinct selected experts of an M > 1 call (written by the W13 kernel,
+// read by the W2 kernel of the same call).
+struct GroupTable {
+    int n_u;
+    int pad_[63];
+    int u_expert[kMaxSlots];
+    unsigned u_mask[kMaxSlots];
+    signed char u_slot[kMaxSlots][kMaxTokens];
+};
+
+// Workspace layout (bytes from the start of ws, 256-byte aligned regions):
+//   [0, kSharedActBytes)                  shared-expert activations [M, Is] fp32
+//   [kGroupOffset, +sizeof(GroupTable))   GroupTable
+//   [kRoutedActOffset, +M*K*I*4)          routed activations [M, K, I] fp32
+constexpr size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+constexpr size_t kSharedActBytes = (size_t)kMaxTokens * kMaxInter * sizeof(float);
+constexpr size_t kGroupOffset = align256(kSharedActBytes);
+constexpr size_t kRoutedActOffset = kGroupOffset + align256(sizeof(GroupTable));
+
+inline int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
+
+hipError_t launch_route(const void *x, const void *wr, int M, int H, int E, int K, int renorm,
+                        int32_t *ids, float *w, float *logits, hipStream_t s);
+hipError_t launch_shared(const void *x, const void *wgu, const void *wd, int M, int H, int Is,
+                         float *s_out, float *act_shared, hipStream_t s);
+hipError_t launch_w13_routed(const void *x, const void *w13, const int32_t *ids, int M, int H,
+                             int E, int I, int K, float *act, GroupTable *table, hipStream_t s);
+hipError_t launch_fused(const void *x, const void *w13, const void *w2, const int32_t *ids,
+                        const float *tw, const float *shared_in, int M, int H, int E, int I, int K,
+                        void *y, float *act, GroupTable *table, hipStream_t s);
+hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids, const float *tw,
+                            const float *shared_in, int M, int H, int E, int I, int K, void *y,
+                            GroupTable *table, hipStream_t s);
+hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s);
+
+} // namespace moe
+
+#endif

@@ -1,0 +1,167 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/moe_decode.h declares, and rejects bad arguments on the host before
+anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from routed_expert_gemv_amd import _lib, build, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+FAKE = 0x10000       # aligned, never dereferenced: validation fails first
+FAKE_ODD = 0x10002   # 2-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:moe_status|int|size_t|const char \*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_library_builds_and_loads():
+    assert os.path.exists(build.LIB) or build.build(force=True)
+    L = _lib.lib()
+    assert L.moe_abi_version() == 1
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"moe_route", "shared_expert", "moe_decode_fused", "moe_workspace_bytes"}
+    L = C.CDLL(build.LIB)
+    for n in names:
+        assert hasattr(L, n), "symbol %s declared in moe_decode.h is not exported" % n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define MOE_ABI_VERSION (\d+)", open(HEADER).read())
+    assert int(m.group(1)) == _lib.lib().moe_abi_version()
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        s = L.moe_status_str(code).decode()
+        assert s and s != "unknown status"
+    assert L.moe_status_str(-99).decode() == "unknown status"
+
+
+def test_workspace_bytes():
+    L = _lib.lib()
+    n = L.moe_workspace_bytes(1, 2048, 256, 512, 8, 512)
+    assert n >= 8 * 512 * 4 and n % 256 == 0
+    assert L.moe_workspace_bytes(8, 2048, 256, 512, 8, 512) >= 8 * 8 * 512 * 4
+    assert L.moe_workspace_bytes(9, 2048, 256, 512, 8, 512) == 0      # M > 8
+    assert L.moe_workspace_bytes(1, 2000, 256, 512, 8, 512) == 0      # H
+    assert L.moe_workspace_bytes(1, 2048, 256, 500, 8, 512) == 0      # I
+    assert L.moe_workspace_bytes(1, 2048, 4, 512, 8, 0) == 0          # K > E
+    assert L.moe_workspace_bytes(8, 4096, 256, 512, 8, 0) == 0        # H = 4096 needs M <= 4
+
+
+def test_route_validation():
+    L = _lib.lib()
+    ok = dict(M=1, H=2048, E=256, K=8)
+
+    def call(x=FAKE, wr=FAKE, ids=FAKE, w=FAKE, lg=FAKE, **kw):
+        a = dict(ok, **kw)
+        return L.moe_route(x, wr, a["M"], a["H"], a["E"], a["K"], 1, ids, w, lg, None)
+
+    assert call(x=None) == -1
+    assert call(lg=None) == -1
+    assert call(H=2000) == -2
+    assert call(M=9) == -2
+    assert call(M=-1) == -2
+    assert call(E=0) == -2
+    assert call(K=17, E=256) == -2
+    assert call(K=9, E=8) == -2
+    assert call(E=1025) == -2
+    assert call(x=FAKE_ODD) == -3
+    assert call(M=0) == 0          # empty call: nothing enqueued
+
+
+def test_shared_expert_validation():
+    L = _lib.lib()
+
+    def call(x=FAKE, gu=FAKE, d=FAKE, s=FAKE, ws=FAKE, M=1, H=2048, Is=512, n=1 << 20):
+        return L.shared_expert(x, gu, d, M, H, Is, s, ws, n, None)
+
+    assert call(d=None) == -1
+    assert call(Is=500) == -2
+    assert call(H=4096, M=8) == -2
+    assert call(gu=FAKE_ODD) == -3
+    assert call(ws=FAKE + 16) == -3
+    assert call(n=100) == -4
+    assert call(M=0) == 0
+
+
+def test_fused_validation():
+    L = _lib.lib()
+    need = L.moe_workspace_bytes(2, 2048, 256, 512, 8, 0)
+
+    def call(x=FAKE, w13=FAKE, w2=FAKE, ids=FAKE, tw=FAKE, sh=None, y=FAKE, ws=FAKE,
+             M=2, H=2048, E=256, I=512, K=8, n=need):
+        return L.moe_decode_fused(x, w13, w2, ids, tw, sh, M, H, E, I, K, y, ws, n, None)
+
+    assert call(w2=None) == -1
+    assert call(y=None) == -1
+    assert call(I=96) == -2
+    assert call(K=0) == -2
+    assert call(w13=FAKE_ODD) == -3
+    assert call(sh=FAKE + 2) == -3
+    assert call(n=need - 1) == -4
+    assert call(M=0) == 0
+
+
+def test_debug_probe_validation():
+    L = _lib.lib()
+    assert L.moe_dbg_wave_sum(None, FAKE, None) == -1
+    assert L.moe_dbg_wave_sum(FAKE + 1, FAKE, None) == -3
+    assert L.moe_dbg_w13_silu(FAKE, FAKE, FAKE, 1, 2048, 256, 512, 8, None, FAKE, 1 << 20,
+                              None) == -1
+    assert L.moe_dbg_w2_combine(FAKE, FAKE, FAKE, FAKE, None, 1, 2048, 256, 512, 8, FAKE, FAKE,
+                                16, None) == -4
+
+
+def test_python_binding_rejects_host_tensors():
+    import routed_expert_gemv_amd as m
+    x = torch.zeros(1, 2048, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        m.moe_route(x, torch.zeros(16, 2048, dtype=torch.float16), 4)
+
+
+def test_generator_is_seeded_and_ordered():
+    sh = synth.LayerShape(M=2, H=512, E=4, K=2, I=64, Is=64)
+    a = synth.draw_layer(sh, 3, "cpu")
+    b = synth.draw_layer(sh, 3, "cpu")
+    c = synth.draw_layer(sh, 4, "cpu")
+    for k in ("wr", "w13", "w2", "wsgu", "wsd", "x"):
+        assert torch.equal(a[k], b[k])
+        assert not torch.equal(a[k], c[k])
+        assert a[k].dtype == torch.float16 and a[k].is_contiguous()
+    assert a["w13"].shape == (4, 128, 512) and a["w2"].shape == (4, 512, 64)
+    assert a["wsgu"].shape == (128, 512) and a["wsd"].shape == (512, 64)
+    # weights ~ N(0, 0.02), x ~ N(0, 1)
+    assert 0.015 < a["w13"].float().std().item() < 0.025
+    assert 0.8 < a["x"].float().std().item() < 1.2
+    x1 = synth.redraw_x(sh, 3, 1, "cpu")
+    assert x1.shape == (2, 512) and not torch.equal(x1, a["x"])
+    assert torch.equal(x1, synth.redraw_x(sh, 3, 1, "cpu"))
+
+
+def test_margin_guard_redraws_until_separated():
+    from tests import cases
+    sh = synth.SHAPES["tiny_e16_k4_i128"]
+    t = cases.draw_case(sh, 0, "cpu")
+    import oracle
+    lg = oracle.router_logits(cases.host64(t["x"]), cases.host64(t["wr"]))
+    _, _, margin = oracle.topk_softmax(lg, sh.K)
+    bound = cases.logit_bound(t, sh).max(axis=-1)
+    # the accepted margin exceeds twice the worst-case fp32 logit error of every token
+    assert np.all(margin > 2 * bound)
+    assert np.all(margin > cases.required_margin(t, sh))
