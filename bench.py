@@ -9,10 +9,14 @@ SiLU*mul, W2 + weighted combine + shared add).  2.08 GB of weights stream per
 replay, far above the 256 MiB last-level cache, so every replay reads cold
 from HBM.  Inputs are seeded synthetic tensors resident in HBM before timing.
 
+Each layer is one launch of the fused layer kernel (moe_layer_decode); with
+--path separate the three entry points run instead (six kernels per layer).
+
 Reported (one JSON line): expert-byte throughput in GB/s (value), us/layer,
 fraction of the 8 TB/s HBM peak, the roofline of the dominant kernel (the
-W13 + SiLU kernel, timed with HIP events on its own stream) and the fp64
-oracle timed on this host's cores on a bounded sample of the same layers.
+fused layer kernel, each launch timed with HIP events on the stream it runs
+on) and the fp64 oracle timed on this host's cores on a bounded sample of the
+same layers.
 """
 from __future__ import annotations
 
@@ -29,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE decode µs/layer and achieved HBM GB/s (% of MI355X peak), M=1"
 HBM_PEAK_GBS = 8000.0
 LAYERS = 36
-COUNTERS = os.path.join(ROOT, "profiles", "w13_counters_full_e256_k8_i512.json")
+COUNTERS = os.path.join(ROOT, "profiles", "layer_kernel_counters_full_e256_k8_i512.json")
 KERNEL_SRC = os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", "moe_kernels.hip")
 
 
@@ -46,15 +50,15 @@ def layer_bytes(sh, n_distinct):
     return expert, total
 
 
-def w13_launch_bytes(sh):
-    """Algorithmic bytes of one routed W13 + SiLU launch at M=1: K experts' gate and
-    up rows, x, and the fp32 activations written."""
-    return sh.K * 2 * sh.I * sh.H * 2 + sh.M * sh.H * 2 + sh.M * sh.K * sh.I * 4
+def launch_bytes(sh):
+    """Algorithmic bytes of one fused layer launch at M=1 (all K experts distinct):
+    router, K experts' W13 and W2 rows, shared expert, x and y."""
+    return layer_bytes(sh, sh.K)[1]
 
 
-def counters_traffic(n_launch_bytes):
-    """HBM traffic of the W13 kernel from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def counters_traffic():
+    """HBM traffic per launch of the fused layer kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source; else None."""
     try:
         c = json.load(open(COUNTERS))
     except (OSError, ValueError):
@@ -102,22 +106,19 @@ def cpu_baseline(stack_tensors, sh, budget_s=12.0):
                       "router, top-k, 8 experts, shared expert), %.1f s wall" % (done, el)}
 
 
-def time_w13(layers, sh, reps):
-    """Average duration of the routed W13 + SiLU kernel, with HIP events recorded
-    around each launch on the stream the kernel runs on (cold: layers rotate)."""
+def time_launches(layers, reps):
+    """Average duration of one layer launch, with HIP events recorded around each
+    launch on the stream the kernel runs on (cold: the 36 layers rotate)."""
     import torch
-    import routed_expert_gemv_amd as moe
 
     stream = torch.cuda.current_stream()
-    acts = [torch.empty((sh.M, sh.K, sh.I), dtype=torch.float32, device="cuda") for _ in layers]
     evs = []
     for r in range(reps + 1):
-        for layer, act in zip(layers, acts):
+        for layer in layers:
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            moe.moe_dbg_w13_silu(layer.t["x"], layer.t["w13"], layer.topk_ids, activated=act,
-                                 ws=layer.ws, stream=stream)
+            layer.forward(stream)
             b.record(stream)
             if r > 0:
                 evs.append((a, b))
@@ -126,16 +127,145 @@ def time_w13(layers, sh, reps):
     return sum(ms) / len(ms) * 1e3, len(ms)  # us, launches
 
 
+# ---------------------------------------------------------------- rocprofv3 helpers
+COPY_BYTES = 1 << 30
+
+
+def counters_pass(args):
+    """Workload for `rocprofv3 --pmc`: a plain 1 GiB device copy (calibrates what
+    FETCH_SIZE / WRITE_SIZE read for a known byte count), then the fused layer
+    kernel on every layer of the stack, twice (cold: layers rotate)."""
+    import torch
+    from routed_expert_gemv_amd import synth
+    from routed_expert_gemv_amd.stack import DecodeLayer
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.float16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    sh = synth.SHAPES["full_e256_k8_i512"]
+    layers = [DecodeLayer(synth.draw_layer(sh, s, dev), sh) for s in range(args.layers)]
+    for _ in range(2):
+        for l in layers:
+            l.forward()
+    torch.cuda.synchronize()
+    log("counters pass done: 3 copies of %d bytes, %d layer launches" % (COPY_BYTES, 2 * len(layers)))
+
+
+def _read_csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir, out_path, cmds):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the W13 kernel, scaled by what the
+    same counters read for the 1 GiB copy, into a JSON summary."""
+    def per_kernel(d, counter):
+        rows = _read_csv_rows(d, "counter_collection.csv")
+        w13, copy = [], []
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            v = float(r["Counter_Value"])
+            name = r.get("Kernel_Name", "")
+            if "k_layer" in name:
+                w13.append(v)
+            elif "copy" in name.lower():
+                copy.append(v)
+        return w13, copy
+
+    fw, fc = per_kernel(fetch_dir, "FETCH_SIZE")
+    ww, wc = per_kernel(write_dir, "WRITE_SIZE")
+    if not fw or not fc or not ww or not wc:
+        raise SystemExit("counter rows missing: fetch %d/%d write %d/%d" % (len(fw), len(fc), len(ww), len(wc)))
+    kib = 1024.0
+    fetch_scale = (sum(fc) / len(fc)) * kib / COPY_BYTES
+    write_scale = (sum(wc) / len(wc)) * kib / COPY_BYTES
+    fetch_b = (sum(fw) / len(fw)) * kib / fetch_scale
+    write_b = (sum(ww) / len(ww)) * kib / write_scale
+    from routed_expert_gemv_amd import synth
+    sh = synth.SHAPES["full_e256_k8_i512"]
+    res = {
+        "kernel": "k_layer<4,64,1,4> (fused layer kernel, M=1)",
+        "workload": "full-width layer H=2048 E=256 K=8 I=512, M=1, 36 layers rotating",
+        "commands": cmds,
+        "fetch_size_kib_per_dispatch": sum(fw) / len(fw),
+        "write_size_kib_per_dispatch": sum(ww) / len(ww),
+        "copy_fetch_kib": sum(fc) / len(fc), "copy_write_kib": sum(wc) / len(wc),
+        "copy_bytes": COPY_BYTES, "fetch_scale": fetch_scale, "write_scale": write_scale,
+        "hbm_bytes_per_dispatch": int(round(fetch_b + write_b)),
+        "algorithmic_bytes_per_dispatch": launch_bytes(sh),
+        "dispatches": len(fw),
+        "kernel_source_sha256": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest(),
+    }
+    with open(out_path, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))
+
+
+def summarize_trace(trace_dir, out_path, cmd):
+    """Kernel-trace summary: per-kernel count / average duration, and the average
+    idle gap between consecutive kernels inside the replayed stack graph."""
+    rows = _read_csv_rows(trace_dir, "kernel_trace.csv")
+    if not rows:
+        raise SystemExit("no kernel_trace.csv under " + trace_dir)
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
+    by = {}
+    for s0, e0, n in ev:
+        by.setdefault(n, []).append(e0 - s0)
+    ours = [e for e in ev if "moe::" in e[2] or "_ZN3moe" in e[2]]
+    gaps = [b[0] - a[1] for a, b in zip(ours, ours[1:]) if 0 <= b[0] - a[1] < 20000]
+    lines = ["# rocprofv3 kernel trace: " + os.path.basename(out_path), "",
+             "Command: `%s`" % cmd, "",
+             "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for n, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        short = n.split("(")[0][:90]
+        lines.append("| `%s` | %d | %.3f | %.3f | %.3f |" % (short, len(d), sum(d) / len(d) / 1e3,
+                                                          min(d) / 1e3, max(d) / 1e3))
+    if gaps:
+        gaps.sort()
+        lines += ["", "Gap between consecutive library kernels (end -> next start, < 20 us): "
+                  "n=%d, median %.3f us, mean %.3f us" % (len(gaps), gaps[len(gaps) // 2] / 1e3,
+                                                       sum(gaps) / len(gaps) / 1e3)]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=LAYERS)
-    ap.add_argument("--w13-reps", type=int, default=5)
+    ap.add_argument("--launch-reps", type=int, default=5)
+    ap.add_argument("--path", choices=("fused", "separate"), default="fused",
+                    help="fused: moe_layer_decode (one launch per layer); separate: the "
+                         "three entry points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--counters-pass", action="store_true",
+                    help="run the rocprofv3 --pmc workload (copy calibration + W13 launches)")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
+    ap.add_argument("--cmd", action="append", default=[],
+                    help="command line(s) recorded in a summary")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, cmds=args.cmd)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, cmd=" && ".join(args.cmd))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode layer is not sharded across GPUs "
@@ -151,12 +281,15 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.counters_pass:
+        counters_pass(args)
+        return
     sh = synth.SHAPES["full_e256_k8_i512"]
 
     log("drawing %d layers (seeds 0..%d) on %s" % (args.layers, args.layers - 1, dev))
     t0 = time.perf_counter()
     tensors = [synth.draw_layer(sh, s, dev) for s in range(args.layers)]
-    layers = [DecodeLayer(t, sh) for t in tensors]
+    layers = [DecodeLayer(t, sh, fused=args.path == "fused") for t in tensors]
     torch.cuda.synchronize()
     log("drawn in %.1f s; capturing the stack graph" % (time.perf_counter() - t0))
     stack = DecodeStack(layers)
@@ -184,11 +317,11 @@ def main():
     gbs_total = total_b / (ms_step * 1e-3) / 1e9
     log("%.3f ms/replay, %.2f us/layer, %.0f GB/s expert bytes" % (ms_step, us_layer, gbs_expert))
 
-    w13_us, n_launch = time_w13(layers, sh, args.w13_reps)
-    w13_b = w13_launch_bytes(sh)
-    w13_gbs = w13_b / (w13_us * 1e-6) / 1e9
-    traffic = counters_traffic(w13_b)
-    log("W13 kernel: %.2f us avg over %d launches, %.0f GB/s" % (w13_us, n_launch, w13_gbs))
+    k_us, n_launch = time_launches(layers, args.launch_reps)
+    k_b = launch_bytes(sh)
+    k_gbs = k_b / (k_us * 1e-6) / 1e9
+    traffic = counters_traffic() if args.path == "fused" else None
+    log("layer launch: %.2f us avg over %d launches, %.0f GB/s" % (k_us, n_launch, k_gbs))
 
     out = {
         "metric": METRIC, "value": round(gbs_expert, 1), "unit": "GB/s",
@@ -197,15 +330,18 @@ def main():
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": "36-layer full-width MoE decode stack as one hipGraph: M=1, "
                                "H=2048, E=256, top-8 renormalised, I=512, shared Is=512, fp16",
-                   "layers": args.layers, "layer_seeds": "0..%d" % (args.layers - 1)},
+                   "layers": args.layers, "layer_seeds": "0..%d" % (args.layers - 1),
+                   "path": args.path},
         "us_per_layer": round(us_layer, 3),
         "frac_of_peak": round(gbs_expert / HBM_PEAK_GBS, 4),
         "gbs_total": round(gbs_total, 1),
         "expert_bytes_per_layer": expert_b // args.layers,
-        "roofline": {"kernel": "k_w13_silu (routed W13 GEMV + SiLU*mul, M=1)", "bound": "hbm",
-                     "achieved": round(w13_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(w13_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_us": round(w13_us, 3), "bytes_per_launch": w13_b},
+        "roofline": {"kernel": ("k_layer (fused layer kernel: router, top-k, W13 + SiLU, "
+                                "W2 + combine, shared expert), M=1" if args.path == "fused"
+                                else "layer = six kernels (three entry points), M=1"),
+                     "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(k_us, 3), "bytes_per_launch": k_b},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -134,7 +134,34 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
                             int M, int H, int E, int I, int K, void *y, void *ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* Steps 1-5, the whole layer: the same results, bit for bit, as
+ *   shared_expert -> moe_route -> moe_decode_fused(shared_in = s)
+ * on one stream, in as few launches as the sizes allow.  For M = 1,
+ * H in {1024, 2048, 4096}, I <= 1024, Is in {0, I} and K*I <= 8192 it is ONE
+ * kernel: workgroups take the router, shared gate/up, routed W13 and routed
+ * W2 roles in that order and hand results on through counters in the
+ * workspace (a workgroup only waits on lower-numbered ones; every wait is
+ * bounded), so routed W2 rows are already streaming while W13 finishes.
+ * Other sizes run the three calls' kernels in sequence.
+ *   x, w_router, w13, w2  as for moe_route / moe_decode_fused
+ *   w_gate_up, w_down     shared expert [2Is, H] / [H, Is], or both NULL (Is ignored)
+ *   topk_ids, topk_w, logits  outputs as for moe_route
+ *   y          [M, H] fp16 out
+ *   ws         >= moe_workspace_bytes(M, H, E, I, K, Is) bytes, ZERO-FILLED before its
+ *              first use with this function; every call leaves its synchronisation
+ *              words at zero again.  Calls that share a ws must not overlap in time.
+ * A wait that exhausts its poll budget (not expected on an idle GPU) is counted
+ * in the workspace; moe_dbg_layer_timeouts reads the count. */
+moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13, const void *w2,
+                            const void *w_gate_up, const void *w_down, int M, int H, int E, int I,
+                            int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
+                            float *logits, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ---- test-only probes (not part of the decode path) --------------------- */
+
+/* Number of bounded waits of moe_layer_decode that gave up, for workspace `ws`,
+ * written to out[0] (device). */
+moe_status moe_dbg_layer_timeouts(const void *ws, unsigned *out, hipStream_t stream);
 
 /* Sums 64 fp32 values with one wavefront's cross-lane (DPP) reduction, the
  * same routine the GEMV kernels use; out[0] = the sum.  in: [64] device. */

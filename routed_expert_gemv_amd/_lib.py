@@ -15,7 +15,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
                 -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
 EXPORTED = ["moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
             "shared_expert", "moe_decode_fused", "moe_dbg_wave_sum", "moe_dbg_w13_silu",
-            "moe_dbg_w2_combine"]
+            "moe_dbg_w2_combine", "moe_layer_decode", "moe_dbg_layer_timeouts"]
 
 _vp = C.c_void_p
 _i = C.c_int
@@ -51,6 +51,11 @@ def lib() -> C.CDLL:
             L.moe_dbg_w2_combine.restype = _i
             L.moe_dbg_w2_combine.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                              _vp, _sz, _vp]
+            L.moe_layer_decode.restype = _i
+            L.moe_layer_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp] + [_i] * 7 + \
+                [_vp, _vp, _vp, _vp, _vp, _sz, _vp]
+            L.moe_dbg_layer_timeouts.restype = _i
+            L.moe_dbg_layer_timeouts.argtypes = [_vp, _vp, _vp]
             _lib = L
     return _lib
 

@@ -57,11 +57,11 @@ def moe_workspace_bytes(M: int, H: int, E: int, I: int, K: int, Is: int = 0) -> 
 
 
 def workspace(M: int, H: int, E: int, I: int, K: int, Is: int = 0, device=None) -> torch.Tensor:
-    """A device workspace big enough for shared_expert and moe_decode_fused."""
+    """A zero-filled device workspace big enough for every entry point at these sizes."""
     n = moe_workspace_bytes(M, H, E, I, K, Is)
     if n == 0:
         raise MoeError("moe_workspace_bytes", -2)
-    return torch.empty(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
+    return torch.zeros(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
 
 
 def moe_route(x, w_router, K: int, renormalize: bool = True, topk_ids=None, topk_w=None,
@@ -202,3 +202,57 @@ def moe_dbg_w2_combine(activated, w2, topk_ids, topk_w, shared_in=None, y=None, 
                                        ws.numel(), _stream(stream, dev))
     _check("moe_dbg_w2_combine", st)
     return y
+
+
+def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int = 8,
+                     renormalize: bool = True, topk_ids=None, topk_w=None, logits=None, y=None,
+                     ws=None, stream=None):
+    """The whole layer (shared expert, routing, routed experts, combine) in as few
+    launches as the sizes allow.  Returns (y, topk_ids, topk_w, logits)."""
+    _dev_tensor("x", x, torch.float16, 2)
+    _dev_tensor("w_router", w_router, torch.float16, 2)
+    _dev_tensor("w13", w13, torch.float16, 3)
+    _dev_tensor("w2", w2, torch.float16, 3)
+    M, H = x.shape
+    E, twoI, H2 = w13.shape
+    I = twoI // 2
+    if H2 != H or w2.shape != (E, H, I) or w_router.shape != (E, H):
+        raise ValueError("layer shapes: router %s, w13 %s, w2 %s for H=%d"
+                         % (tuple(w_router.shape), tuple(w13.shape), tuple(w2.shape), H))
+    Is = 0
+    if w_gate_up is not None or w_down is not None:
+        _dev_tensor("w_gate_up", w_gate_up, torch.float16, 2)
+        _dev_tensor("w_down", w_down, torch.float16, 2)
+        Is = w_gate_up.shape[0] // 2
+        if w_gate_up.shape != (2 * Is, H) or w_down.shape != (H, Is):
+            raise ValueError("shared expert shapes: gate_up %s, down %s"
+                             % (tuple(w_gate_up.shape), tuple(w_down.shape)))
+    dev = x.device
+    topk_ids = torch.empty((M, K), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
+    topk_w = torch.empty((M, K), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    logits = torch.empty((M, E), dtype=torch.float32, device=dev) if logits is None else logits
+    y = torch.empty((M, H), dtype=torch.float16, device=dev) if y is None else y
+    for name, t, dt, n in (("topk_ids", topk_ids, torch.int32, M * K),
+                           ("topk_w", topk_w, torch.float32, M * K),
+                           ("logits", logits, torch.float32, M * E), ("y", y, torch.float16, M * H)):
+        _dev_tensor(name, t, dt)
+        if t.numel() != n:
+            raise ValueError("%s must have %d elements" % (name, n))
+    if ws is None:
+        ws = workspace(max(M, 1), H, E, I, K, Is, dev)
+    _dev_tensor("ws", ws, torch.uint8)
+    st = _lib.lib().moe_layer_decode(_ptr(x), _ptr(w_router), _ptr(w13), _ptr(w2), _ptr(w_gate_up),
+                                     _ptr(w_down), M, H, E, I, K, Is, int(bool(renormalize)),
+                                     _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y), _ptr(ws),
+                                     ws.numel(), _stream(stream, dev))
+    _check("moe_layer_decode", st)
+    return y, topk_ids, topk_w, logits
+
+
+def moe_dbg_layer_timeouts(ws, stream=None) -> int:
+    """Test probe: how many bounded waits of moe_layer_decode gave up on this workspace."""
+    _dev_tensor("ws", ws, torch.uint8)
+    out = torch.zeros(1, dtype=torch.int32, device=ws.device)
+    st = _lib.lib().moe_dbg_layer_timeouts(_ptr(ws), _ptr(out), _stream(stream, ws.device))
+    _check("moe_dbg_layer_timeouts", st)
+    return int(out.item())

@@ -93,6 +93,51 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
                                    reinterpret_cast<GroupTable *>(base + kGroupOffset), stream));
 }
 
+moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13, const void *w2,
+                            const void *w_gate_up, const void *w_down, int M, int H, int E, int I,
+                            int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
+                            float *logits, void *y, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    const bool shared = w_gate_up != nullptr || w_down != nullptr;
+    if (!shared) Is = 0;
+    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (shared && !i_ok(Is)))
+        return MOE_ERR_SHAPE;
+    if (M == 0) return MOE_OK;
+    if (!x || !w_router || !w13 || !w2 || !topk_ids || !topk_w || !logits || !y || !ws ||
+        (shared && (!w_gate_up || !w_down)))
+        return MOE_ERR_NULL;
+    if (!al(x, 16) || !al(w_router, 16) || !al(w13, 16) || !al(w2, 16) || !al(topk_ids, 4) ||
+        !al(topk_w, 4) || !al(logits, 4) || !al(y, 2) || !al(ws, 256) ||
+        (shared && (!al(w_gate_up, 16) || !al(w_down, 16))))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < routed_ws_bytes(M, I, K)) return MOE_ERR_WORKSPACE;
+    char *base = static_cast<char *>(ws);
+    float *act_s = reinterpret_cast<float *>(base);
+    float *act = reinterpret_cast<float *>(base + kRoutedActOffset);
+    if (layer_fusable(M, H, E, I, K, Is))
+        return hip_status(launch_layer(x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is,
+                                       renormalize, topk_ids, topk_w, logits, y, act, act_s,
+                                       reinterpret_cast<LayerSync *>(base + kSyncOffset), stream));
+    float *s_out = shared ? reinterpret_cast<float *>(base + kSharedOutOffset) : nullptr;
+    hipError_t err = hipSuccess;
+    if (shared) err = launch_shared(x, w_gate_up, w_down, M, H, Is, s_out, act_s, stream);
+    if (err == hipSuccess)
+        err = launch_route(x, w_router, M, H, E, K, renormalize, topk_ids, topk_w, logits, stream);
+    if (err == hipSuccess)
+        err = launch_fused(x, w13, w2, topk_ids, topk_w, s_out, M, H, E, I, K, y, act,
+                           reinterpret_cast<GroupTable *>(base + kGroupOffset), stream);
+    return hip_status(err);
+}
+
+moe_status moe_dbg_layer_timeouts(const void *ws, unsigned *out, hipStream_t stream)
+{
+    if (!ws || !out) return MOE_ERR_NULL;
+    if (!al(ws, 256) || !al(out, 4)) return MOE_ERR_ALIGN;
+    const char *base = static_cast<const char *>(ws);
+    return hip_status(launch_read_timeouts(reinterpret_cast<const LayerSync *>(base + kSyncOffset),
+                                           out, stream));
+}
+
 moe_status moe_dbg_wave_sum(const float *in, float *out, hipStream_t stream)
 {
     if (!in || !out) return MOE_ERR_NULL;

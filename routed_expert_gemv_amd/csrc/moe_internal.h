@@ -25,14 +25,35 @@ struct GroupTable {
     signed char u_slot[kMaxSlots][kMaxTokens];
 };
 
+// Synchronisation words of the fused layer kernel, one per 256-byte line.
+constexpr int kW13Counters = 8;
+struct alignas(256) SyncWord {
+    unsigned v;
+};
+struct LayerSync {
+    SyncWord router_done;                // router blocks that published their logits
+    SyncWord shared_done;                // shared gate/up blocks that published act_s
+    SyncWord w13_done[kW13Counters];     // routed W13 blocks that published act
+    SyncWord blocks_done;                // finished blocks (the last one re-arms)
+    SyncWord timeouts;                   // bounded waits that gave up (diagnostic)
+};
+
+// The fused kernel stages K*I routed and Is shared activations (fp32) in LDS.
+constexpr int kFusedMaxAct = 8192;
+
 // Workspace layout (bytes from the start of ws, 256-byte aligned regions):
 //   [0, kSharedActBytes)                  shared-expert activations [M, Is] fp32
 //   [kGroupOffset, +sizeof(GroupTable))   GroupTable
+//   [kSyncOffset, +sizeof(LayerSync))     LayerSync (zero before first use)
+//   [kSharedOutOffset, +M*H*4)            shared-expert output [M, H] fp32
 //   [kRoutedActOffset, +M*K*I*4)          routed activations [M, K, I] fp32
 constexpr size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 constexpr size_t kSharedActBytes = (size_t)kMaxTokens * kMaxInter * sizeof(float);
 constexpr size_t kGroupOffset = align256(kSharedActBytes);
-constexpr size_t kRoutedActOffset = kGroupOffset + align256(sizeof(GroupTable));
+constexpr size_t kSyncOffset = kGroupOffset + align256(sizeof(GroupTable));
+constexpr size_t kSharedOutOffset = kSyncOffset + align256(sizeof(LayerSync));
+constexpr size_t kSharedOutBytes = (size_t)kMaxTokens * 4096 * sizeof(float);
+constexpr size_t kRoutedActOffset = kSharedOutOffset + align256(kSharedOutBytes);
 
 inline int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
@@ -48,6 +69,12 @@ hipError_t launch_fused(const void *x, const void *w13, const void *w2, const in
 hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids, const float *tw,
                             const float *shared_in, int M, int H, int E, int I, int K, void *y,
                             GroupTable *table, hipStream_t s);
+bool layer_fusable(int M, int H, int E, int I, int K, int Is);
+hipError_t launch_layer(const void *x, const void *wr, const void *w13, const void *w2,
+                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
+                        int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
+                        float *act_s, LayerSync *sync, hipStream_t s);
+hipError_t launch_read_timeouts(const LayerSync *sync, unsigned *out, hipStream_t s);
 hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s);
 
 } // namespace moe

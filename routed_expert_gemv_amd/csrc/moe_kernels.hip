@@ -190,8 +190,34 @@ __device__ __forceinline__ void group_store(const GroupScan<MT> &g, GroupTable *
 }
 
 // ---------------------------------------------------------------- router GEMV
+// Lane l holds 16-byte chunks c*64 + l of a 2048-wide (H = 512*HC) row.
+template <int HC>
+__device__ __forceinline__ void load_row(const f16 *row, f16x8 (&w)[HC])
+{
+    const f16x8 *r = reinterpret_cast<const f16x8 *>(row);
+#pragma unroll
+    for (int c = 0; c < HC; ++c) w[c] = stream_load(r + c * kWave + lane_id());
+}
+
+template <int HC>
+__device__ __forceinline__ void load_x(const f16 *xrow, f16x8 (&xv)[HC])
+{
+    const f16x8 *r = reinterpret_cast<const f16x8 *>(xrow);
+#pragma unroll
+    for (int c = 0; c < HC; ++c) xv[c] = r[c * kWave + lane_id()];
+}
+
+// sum over the row of w * x: per-lane v_dot2 chain over its chunks, then the wave tree
+template <int HC>
+__device__ __forceinline__ float row_dot(const f16x8 (&w)[HC], const f16x8 (&xv)[HC])
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < HC; ++c) acc = dot8(w[c], xv[c], acc);
+    return wave_sum(acc);
+}
+
 // One wave per expert row e: logits[m, e] = sum_h Wr[e, h] x[m, h].
-// Lane l holds 16-byte chunks c*64 + l of the row (c < HC, H = 512*HC).
 template <int HC>
 __global__ __launch_bounds__(kWave) void k_router(const f16 *__restrict__ x,
                                                   const f16 *__restrict__ wr, int M, int E,
@@ -199,81 +225,147 @@ __global__ __launch_bounds__(kWave) void k_router(const f16 *__restrict__ x,
 {
     constexpr int H = 512 * HC;
     const int e = blockIdx.x;
-    const int lane = lane_id();
-    const f16x8 *row = reinterpret_cast<const f16x8 *>(wr + (size_t)e * H);
     f16x8 w[HC];
-#pragma unroll
-    for (int c = 0; c < HC; ++c) w[c] = stream_load(row + c * kWave + lane);
+    load_row<HC>(wr + (size_t)e * H, w);
     for (int m = 0; m < M; ++m) {
-        const f16x8 *xr = reinterpret_cast<const f16x8 *>(x + (size_t)m * H);
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < HC; ++c) acc = dot8(w[c], xr[c * kWave + lane], acc);
-        const float t = wave_sum(acc);
-        if (lane == 0) logits[(size_t)m * E + e] = t;
+        f16x8 xv[HC];
+        load_x<HC>(x + (size_t)m * H, xv);
+        const float t = row_dot<HC>(w, xv);
+        if (lane_id() == 0) logits[(size_t)m * E + e] = t;
     }
 }
 
 // ---------------------------------------------------------------- top-k + softmax
-// One wave per token.  Key = order-preserving map of the fp32 logit in the
-// high word, ~expert_id in the low word: the largest key is the largest logit,
-// and among equal logits the lower id.  K rounds of a wave arg-max.
-__device__ __forceinline__ uint64_t topk_key(float v, int e)
+// One wave selects for one token.  A finite fp32 logit maps to an
+// order-preserving non-zero uint32 key (0 marks "no entry"); K rounds of a
+// wave-wide DPP max find the largest remaining key, and a ballot over the
+// lane's slots (slot i holds expert i*64 + lane) picks the lowest expert id
+// holding it, so equal logits order by the lower id.
+__device__ __forceinline__ uint32_t order_key(float v)
 {
     v = v + 0.0f; // -0 -> +0, so the two zeros tie
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__global__ __launch_bounds__(kWave) void k_topk(const float *__restrict__ logits, int E, int K,
-                                                int renormalize, int32_t *__restrict__ ids,
-                                                float *__restrict__ weights)
+__device__ __forceinline__ float key_value(uint32_t k)
 {
-    constexpr int NPL = kMaxExperts / kWave;
-    const int m = blockIdx.x;
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __builtin_bit_cast(float, u);
+}
+
+template <int DPP_CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_CTRL, ROW_MASK, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = umax(v, dpp_u32<0xB1, 0xF>(v));
+    v = umax(v, dpp_u32<0x4E, 0xF>(v));
+    v = umax(v, dpp_u32<0x141, 0xF>(v));
+    v = umax(v, dpp_u32<0x140, 0xF>(v));
+    v = umax(v, dpp_u32<0x142, 0xA>(v));
+    v = umax(v, dpp_u32<0x143, 0xC>(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Loads of data another workgroup of the same launch published: agent-scope
+// coherent (they bypass stale cache lines without a cache-wide invalidate).
+__device__ __forceinline__ float ld_agent(const float *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void st_agent(float *p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool COHERENT>
+__device__ __forceinline__ float ld_logit(const float *p)
+{
+    return COHERENT ? ld_agent(p) : *p;
+}
+
+// Top-K of the E <= 64*NPL logits L[0..E).  Lane k < K receives the k-th
+// selected expert id and its logit; returns the largest logit (wave-uniform).
+// COHERENT: L was written by other workgroups of the same launch.
+template <int NPL, bool COHERENT = false>
+__device__ __forceinline__ float wave_topk(const float *__restrict__ L, int E, int K, int &my_id,
+                                           float &my_l)
+{
     const int lane = lane_id();
-    const float *L = logits + (size_t)m * E;
-    uint64_t key[NPL];
+    uint32_t key[NPL];
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
         const int e = i * kWave + lane;
-        key[i] = e < E ? topk_key(L[e], e) : 0ull;
+        key[i] = e < E ? order_key(ld_logit<COHERENT>(L + e)) : 0u;
     }
-    int my_id = 0;
-    float my_l = 0.0f, lmax = 0.0f;
+    float lmax = 0.0f;
+    my_id = 0;
+    my_l = 0.0f;
     for (int k = 0; k < K; ++k) {
-        uint64_t best = 0;
+        uint32_t m = 0u;
 #pragma unroll
-        for (int i = 0; i < NPL; ++i) best = key[i] > best ? key[i] : best;
+        for (int i = 0; i < NPL; ++i) m = umax(m, key[i]);
+        m = wave_max_u32(m);
+        int id = -1;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint64_t o = __shfl_xor(best, off);
-            best = o > best ? o : best;
+        for (int i = 0; i < NPL; ++i) {
+            const uint64_t b = __ballot(key[i] == m);
+            if (id < 0 && b != 0ull) id = i * kWave + __builtin_ctzll(b);
         }
 #pragma unroll
         for (int i = 0; i < NPL; ++i)
-            if (key[i] == best) key[i] = 0ull;
-        const int id = (int)(0xFFFFFFFFu - (uint32_t)best);
-        const float lv = L[id];
+            if (i * kWave + lane == id) key[i] = 0u;
+        const float lv = key_value(m);
         if (k == 0) lmax = lv;
         if (lane == k) {
             my_id = id;
             my_l = lv;
         }
     }
+    return lmax;
+}
+
+// Routing weight of the slot held by this lane (valid in lanes < K): softmax
+// over the selected logits (renormalize) or over all E logits.
+template <bool COHERENT = false>
+__device__ __forceinline__ float topk_weight(const float *__restrict__ L, int E, int K,
+                                             int renormalize, float my_l, float lmax)
+{
+    const int lane = lane_id();
     const float ex = lane < K ? expf(my_l - lmax) : 0.0f;
     float z;
     if (renormalize) {
         z = wave_sum(ex);
     } else {
         float part = 0.0f;
-        for (int e = lane; e < E; e += kWave) part += expf(L[e] - lmax);
+        for (int e = lane; e < E; e += kWave) part += expf(ld_logit<COHERENT>(L + e) - lmax);
         z = wave_sum(part);
     }
+    return ex / z;
+}
+
+template <int NPL>
+__global__ __launch_bounds__(kWave) void k_topk(const float *__restrict__ logits, int E, int K,
+                                                int renormalize, int32_t *__restrict__ ids,
+                                                float *__restrict__ weights)
+{
+    const int m = blockIdx.x;
+    const int lane = lane_id();
+    const float *L = logits + (size_t)m * E;
+    int my_id;
+    float my_l;
+    const float lmax = wave_topk<NPL>(L, E, K, my_id, my_l);
+    const float w = topk_weight(L, E, K, renormalize, my_l, lmax);
     if (lane < K) {
         ids[(size_t)m * K + lane] = my_id;
-        weights[(size_t)m * K + lane] = ex / z;
+        weights[(size_t)m * K + lane] = w;
     }
 }
 
@@ -339,19 +431,28 @@ __global__ __launch_bounds__(kBlock) void k_w13_silu(const f16 *__restrict__ x,
 #pragma unroll
     for (int m = 0; m < MT; ++m)
         if (mask & (1u << m)) {
-            float ag = 0.0f, au = 0.0f;
-#pragma unroll
-            for (int c = 0; c < HC; ++c) {
-                ag = dot8(wg[c], xv[m][c], ag);
-                au = dot8(wu[c], xv[m][c], au);
-            }
-            const float g = wave_sum(ag);
-            const float up = wave_sum(au);
+            const float g = row_dot<HC>(wg, xv[m]);
+            const float up = row_dot<HC>(wu, xv[m]);
             if (lane == 0) act[((size_t)m * K + slot[m]) * I + j] = silu_mul(g, up);
         }
 }
 
 // ---------------------------------------------------------------- W2 + combine
+// d + sum_i w[i] * a[i] over one 16-byte chunk of a W2 row (8 fp16 weights)
+// and the matching 8 fp32 activations, in element order.
+__device__ __forceinline__ float dot8_f32(f16x8 w, f32x4 a0, f32x4 a1, float d)
+{
+    d = fmaf((float)w[0], a0[0], d);
+    d = fmaf((float)w[1], a0[1], d);
+    d = fmaf((float)w[2], a0[2], d);
+    d = fmaf((float)w[3], a0[3], d);
+    d = fmaf((float)w[4], a1[0], d);
+    d = fmaf((float)w[5], a1[1], d);
+    d = fmaf((float)w[6], a1[2], d);
+    d = fmaf((float)w[7], a1[3], d);
+    return d;
+}
+
 // A wave owns RPL = 64/LPR consecutive output rows h; LPR lanes share one
 // row, each holding CPL 16-byte chunks of it (I = 8*LPR*CPL).  For every
 // selected expert (routing order; for M > 1 the distinct experts in order of
@@ -418,16 +519,7 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
 #pragma unroll
                         for (int c = 0; c < CPL; ++c) {
                             const f32x4 *ap = reinterpret_cast<const f32x4 *>(a + (c * LPR + cl) * 8);
-                            const f32x4 a0 = ap[0], a1 = ap[1];
-                            const f16x8 wc = wv[t][c];
-                            d = fmaf((float)wc[0], a0[0], d);
-                            d = fmaf((float)wc[1], a0[1], d);
-                            d = fmaf((float)wc[2], a0[2], d);
-                            d = fmaf((float)wc[3], a0[3], d);
-                            d = fmaf((float)wc[4], a1[0], d);
-                            d = fmaf((float)wc[5], a1[1], d);
-                            d = fmaf((float)wc[6], a1[2], d);
-                            d = fmaf((float)wc[7], a1[3], d);
+                            d = dot8_f32(wv[t][c], ap[0], ap[1], d);
                         }
                         acc[m] = fmaf(wt, d, acc[m]);
                     }
@@ -448,6 +540,314 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
             }
         }
     }
+}
+
+
+// ---------------------------------------------------------------- fused layer (M = 1)
+// The whole layer in one launch.  Workgroups of 16 waves take roles by block
+// index, in dependency order:
+//   [0, nR)            router: one wave per expert row -> logits
+//   [.., +nS)          shared expert gate/up + SiLU*mul -> act_s
+//   [.., +nW13)        routed W13 + SiLU*mul: waits for the router, selects the
+//                      experts itself (every wave runs the same top-k), -> act
+//   [.., +nW2)         routed W2 + combine + shared down: selects the experts,
+//                      issues its W2 (and shared down) row loads, then waits
+//                      for every W13 / shared gate-up block, stages the
+//                      activations in LDS and produces y.
+// A block only waits on blocks with lower indices.  Blocks are dispatched in
+// index order on each XCD, so the lowest unfinished block can always run:
+// the waits cannot deadlock whatever the occupancy.  Every wait is bounded
+// (kSpinLimit polls); a wait that gives up bumps sync->timeouts and goes on,
+// so every wave exits.  The last block to finish re-arms the counters for the
+// next launch (the workspace's sync words start at zero and end at zero).
+//
+// Hand-off without cache-wide fences: data read by other blocks (logits,
+// act, act_s) is stored and loaded with agent-scope coherent accesses; each
+// wave drains its stores (s_waitcnt) before the block barrier, after which
+// one thread bumps the counter.  A waiting block's thread 0 polls with
+// exponential back-off, then the block barrier releases its waves.
+//
+// Arithmetic per element is the same device code as the separate kernels, so
+// the results equal shared_expert + moe_route + moe_decode_fused bit for bit.
+constexpr unsigned kSpinLimit = 1u << 17; // ~0.1 s of polling at most
+constexpr int kLayerWaves = 16;
+constexpr int kLayerBlock = kLayerWaves * kWave;
+
+struct LayerArgs {
+    const f16 *x, *wr, *w13, *w2, *wsgu, *wsd;
+    int E, I, K, Is, renormalize;
+    int nR, nS, nW13, nW2;
+    float *logits;
+    int32_t *ids;
+    float *weights;
+    float *act;
+    float *act_s;
+    f16 *y;
+    LayerSync *sync;
+};
+
+__device__ __forceinline__ unsigned ld_relaxed(const unsigned *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// thread 0 polls until sum(counters[0..n)) >= target and other >= target2
+__device__ __forceinline__ void block_wait(const SyncWord *counters, int n, unsigned target,
+                                           const SyncWord *other, unsigned target2,
+                                           LayerSync *sync)
+{
+    if (threadIdx.x == 0) {
+        unsigned it = 0, nap = 1;
+        for (; it < kSpinLimit; ++it) {
+            unsigned sum = 0;
+            for (int i = 0; i < n; ++i) sum += ld_relaxed(&counters[i].v);
+            if (sum >= target && (other == nullptr || ld_relaxed(&other->v) >= target2)) break;
+            if (nap == 1) __builtin_amdgcn_s_sleep(1);
+            else if (nap == 2) __builtin_amdgcn_s_sleep(2);
+            else __builtin_amdgcn_s_sleep(4);
+            nap = nap < 4 ? nap + 1 : nap;
+        }
+        if (it == kSpinLimit)
+            __hip_atomic_fetch_add(&sync->timeouts.v, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+}
+
+// every wave's agent-coherent stores have completed; then count the block
+__device__ __forceinline__ void block_signal(SyncWord *counter)
+{
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(&counter->v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void block_finish(LayerSync *sync, unsigned total)
+{
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = __hip_atomic_fetch_add(&sync->blocks_done.v, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (old == total - 1) {
+            // every block of this launch is past its waits: re-arm for the next one
+            __hip_atomic_store(&sync->router_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sync->shared_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < kW13Counters; ++i)
+                __hip_atomic_store(&sync->w13_done[i].v, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sync->blocks_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+__device__ __forceinline__ int layer_wave() { return (int)(threadIdx.x / kWave); }
+
+// agent-coherent 16-byte load (data published by another block of this launch)
+__device__ __forceinline__ f32x4 ld_agent4(const float *p)
+{
+    f32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
+                 : "=v"(v)
+                 : "v"(p)
+                 : "memory");
+    return v;
+}
+
+// Routing for the whole block: wave 0 reads the published logits and selects;
+// lane k of every wave then holds the k-th expert id and weight.
+template <int NPL>
+__device__ __forceinline__ void block_route(const LayerArgs &a, int *sh_ids, float *sh_w,
+                                            int &my_id, float &my_w)
+{
+    if (layer_wave() == 0) {
+        float my_l;
+        const float lmax = wave_topk<NPL, true>(a.logits, a.E, a.K, my_id, my_l);
+        my_w = topk_weight<true>(a.logits, a.E, a.K, a.renormalize, my_l, lmax);
+        if (lane_id() < a.K) {
+            sh_ids[lane_id()] = my_id;
+            sh_w[lane_id()] = my_w;
+        }
+    }
+    __syncthreads();
+    const int k = lane_id() < a.K ? lane_id() : 0;
+    my_id = sh_ids[k];
+    my_w = sh_w[k];
+}
+
+template <int HC>
+__device__ __forceinline__ void role_router(const LayerArgs &a, int b)
+{
+    constexpr int H = 512 * HC;
+    const int e = b * kLayerWaves + layer_wave();
+    if (e < a.E) {
+        f16x8 w[HC], xv[HC];
+        load_x<HC>(a.x, xv);
+        load_row<HC>(a.wr + (size_t)e * H, w);
+        const float t = row_dot<HC>(w, xv);
+        if (lane_id() == 0) st_agent(a.logits + e, t);
+    }
+    block_signal(&a.sync->router_done);
+}
+
+template <int HC>
+__device__ __forceinline__ void role_shared_gate_up(const LayerArgs &a, int b)
+{
+    constexpr int H = 512 * HC;
+    const int j = b * kLayerWaves + layer_wave();
+    f16x8 xv[HC], wg[HC], wu[HC];
+    load_x<HC>(a.x, xv);
+    load_row<HC>(a.wsgu + (size_t)j * H, wg);
+    load_row<HC>(a.wsgu + (size_t)(a.Is + j) * H, wu);
+    const float g = row_dot<HC>(wg, xv);
+    const float up = row_dot<HC>(wu, xv);
+    if (lane_id() == 0) st_agent(a.act_s + j, silu_mul(g, up));
+    block_signal(&a.sync->shared_done);
+}
+
+template <int HC, int NPL>
+__device__ __forceinline__ void role_w13(const LayerArgs &a, int b, int *sh_ids, float *sh_w)
+{
+    constexpr int H = 512 * HC;
+    const int per_expert = a.I / kLayerWaves;
+    const int u = b / per_expert;
+    const int j = (b % per_expert) * kLayerWaves + layer_wave();
+    f16x8 xv[HC];
+    load_x<HC>(a.x, xv);
+    block_wait(&a.sync->router_done, 1, (unsigned)a.nR, nullptr, 0u, a.sync);
+    int my_id;
+    float my_w;
+    block_route<NPL>(a, sh_ids, sh_w, my_id, my_w);
+    const int expert = __builtin_amdgcn_readlane(my_id, u);
+    const f16 *base = a.w13 + (size_t)expert * 2 * a.I * H;
+    f16x8 wg[HC], wu[HC];
+    load_row<HC>(base + (size_t)j * H, wg);
+    load_row<HC>(base + (size_t)(a.I + j) * H, wu);
+    const float g = row_dot<HC>(wg, xv);
+    const float up = row_dot<HC>(wu, xv);
+    if (lane_id() == 0) st_agent(a.act + (size_t)u * a.I + j, silu_mul(g, up));
+    block_signal(&a.sync->w13_done[b % kW13Counters]);
+}
+
+template <int LPR, int CPL, int NPL>
+__device__ __forceinline__ void role_w2(const LayerArgs &a, int b, float *lds, int *sh_ids,
+                                        float *sh_w)
+{
+    constexpr int RPL = kWave / LPR;
+    constexpr int BATCH = 8;
+    const int H = a.nW2 * kLayerWaves * RPL;
+    const int lane = lane_id();
+    const int wave = layer_wave();
+    const int r = lane / LPR;
+    const int cl = lane % LPR;
+    const int h = (b * kLayerWaves + wave) * RPL + r;
+    const bool shared = a.nS > 0;
+
+    // shared down rows do not depend on routing: load them first
+    f16x8 ws[CPL];
+    if (shared) {
+        const f16x8 *row = reinterpret_cast<const f16x8 *>(a.wsd + (size_t)h * a.Is);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) ws[c] = stream_load(row + c * LPR + cl);
+    }
+    block_wait(&a.sync->router_done, 1, (unsigned)a.nR, nullptr, 0u, a.sync);
+    int my_id;
+    float my_w;
+    block_route<NPL>(a, sh_ids, sh_w, my_id, my_w);
+    if (b == 0 && wave == 0 && lane < a.K) {
+        a.ids[lane] = my_id;
+        a.weights[lane] = my_w;
+    }
+    // first batch of routed W2 rows in flight before the wait for the activations
+    f16x8 wv[BATCH][CPL];
+    const int first = a.K < BATCH ? a.K : BATCH;
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t)
+        if (t < first) {
+            const int e = __builtin_amdgcn_readlane(my_id, t);
+            const f16x8 *row = reinterpret_cast<const f16x8 *>(a.w2 + ((size_t)e * H + h) * a.I);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
+        }
+    block_wait(a.sync->w13_done, kW13Counters, (unsigned)a.nW13, shared ? &a.sync->shared_done : nullptr,
+               (unsigned)a.nS, a.sync);
+    // stage act [K, I] and act_s [Is] in LDS
+    const int n_act = a.K * a.I;
+    for (int i = threadIdx.x * 4; i < n_act; i += kLayerBlock * 4)
+        *reinterpret_cast<f32x4 *>(lds + i) = ld_agent4(a.act + i);
+    if (shared)
+        for (int i = threadIdx.x * 4; i < a.Is; i += kLayerBlock * 4)
+            *reinterpret_cast<f32x4 *>(lds + n_act + i) = ld_agent4(a.act_s + i);
+    __syncthreads();
+
+    float acc = 0.0f;
+    for (int u0 = 0; u0 < a.K; u0 += BATCH) {
+        const int cnt = a.K - u0 < BATCH ? a.K - u0 : BATCH;
+        if (u0 > 0) {
+#pragma unroll
+            for (int t = 0; t < BATCH; ++t)
+                if (t < cnt) {
+                    const int e = __builtin_amdgcn_readlane(my_id, u0 + t);
+                    const f16x8 *row =
+                        reinterpret_cast<const f16x8 *>(a.w2 + ((size_t)e * H + h) * a.I);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < BATCH; ++t)
+            if (t < cnt) {
+                const int k = u0 + t;
+                const float wt = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), k));
+                const float *ak = lds + (size_t)k * a.I;
+                float d = 0.0f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const f32x4 *ap = reinterpret_cast<const f32x4 *>(ak + (c * LPR + cl) * 8);
+                    d = dot8_f32(wv[t][c], ap[0], ap[1], d);
+                }
+                acc = fmaf(wt, d, acc);
+            }
+    }
+    float acc_s = 0.0f;
+    if (shared) {
+        const float *as = lds + n_act;
+        float d = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(as + (c * LPR + cl) * 8);
+            d = dot8_f32(ws[c], ap[0], ap[1], d);
+        }
+        acc_s = fmaf(1.0f, d, 0.0f);
+    }
+    const float t = group_sum<LPR>(acc);
+    const float ts = group_sum<LPR>(acc_s);
+    if (lane == group_holder<LPR>(r)) a.y[h] = (f16)(shared ? t + ts : t);
+}
+
+template <int HC, int LPR, int CPL, int NPL>
+__global__ __launch_bounds__(kLayerBlock) void k_layer(LayerArgs a)
+{
+    extern __shared__ float lds[];
+    __shared__ int sh_ids[kMaxTopk];
+    __shared__ float sh_w[kMaxTopk];
+    const int b = blockIdx.x;
+    const int total = a.nR + a.nS + a.nW13 + a.nW2;
+    if (b < a.nR)
+        role_router<HC>(a, b);
+    else if (b < a.nR + a.nS)
+        role_shared_gate_up<HC>(a, b - a.nR);
+    else if (b < a.nR + a.nS + a.nW13)
+        role_w13<HC, NPL>(a, b - a.nR - a.nS, sh_ids, sh_w);
+    else
+        role_w2<LPR, CPL, NPL>(a, b - a.nR - a.nS - a.nW13, lds, sh_ids, sh_w);
+    block_finish(a.sync, (unsigned)total);
+}
+
+__global__ void k_read_timeouts(const LayerSync *__restrict__ sync, unsigned *__restrict__ out)
+{
+    if (threadIdx.x == 0) out[0] = ld_relaxed(&sync->timeouts.v);
 }
 
 // ---------------------------------------------------------------- group table only
@@ -492,7 +892,13 @@ hipError_t launch_route(const void *x, const void *wr, int M, int H, int E, int 
     default: return hipErrorInvalidValue;
     }
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_topk, dim3(M), dim3(kWave), 0, s, logits, E, K, renorm, ids, w);
+    if (E <= kWave)
+        hipLaunchKernelGGL(k_topk<1>, dim3(M), dim3(kWave), 0, s, logits, E, K, renorm, ids, w);
+    else if (E <= 4 * kWave)
+        hipLaunchKernelGGL(k_topk<4>, dim3(M), dim3(kWave), 0, s, logits, E, K, renorm, ids, w);
+    else
+        hipLaunchKernelGGL(k_topk<kMaxExperts / kWave>, dim3(M), dim3(kWave), 0, s, logits, E, K,
+                           renorm, ids, w);
     return last();
 }
 
@@ -623,6 +1029,85 @@ hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids
 hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s)
 {
     hipLaunchKernelGGL(k_dbg_wave_sum, dim3(1), dim3(kWave), 0, s, in, out);
+    return last();
+}
+
+
+// ---------------------------------------------------------------- fused layer launcher
+bool layer_fusable(int M, int H, int E, int I, int K, int Is)
+{
+    return M == 1 && (H == 1024 || H == 2048 || H == 4096) && I <= 1024 &&
+           (Is == 0 || Is == I) && K * I <= kFusedMaxAct;
+}
+
+template <int HC, int LPR, int CPL>
+static hipError_t launch_layer_t(const LayerArgs &a, hipStream_t s)
+{
+    const int blocks = a.nR + a.nS + a.nW13 + a.nW2;
+    const size_t lds = (size_t)(a.K * a.I + a.Is) * sizeof(float);
+    if (a.E <= kWave)
+        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, 1>), dim3(blocks), dim3(kLayerBlock), lds, s, a);
+    else if (a.E <= 4 * kWave)
+        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, 4>), dim3(blocks), dim3(kLayerBlock), lds, s, a);
+    else
+        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, kMaxExperts / kWave>), dim3(blocks),
+                           dim3(kLayerBlock), lds, s, a);
+    return last();
+}
+
+template <int HC>
+static hipError_t launch_layer_h(const LayerArgs &a, hipStream_t s)
+{
+    switch (a.I) {
+    case 64: return launch_layer_t<HC, 8, 1>(a, s);
+    case 128: return launch_layer_t<HC, 16, 1>(a, s);
+    case 256: return launch_layer_t<HC, 32, 1>(a, s);
+    case 512: return launch_layer_t<HC, 64, 1>(a, s);
+    case 1024: return launch_layer_t<HC, 64, 2>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_layer(const void *x, const void *wr, const void *w13, const void *w2,
+                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
+                        int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
+                        float *act_s, LayerSync *sync, hipStream_t s)
+{
+    LayerArgs a;
+    a.x = (const f16 *)x;
+    a.wr = (const f16 *)wr;
+    a.w13 = (const f16 *)w13;
+    a.w2 = (const f16 *)w2;
+    a.wsgu = (const f16 *)wsgu;
+    a.wsd = (const f16 *)wsd;
+    a.E = E;
+    a.I = I;
+    a.K = K;
+    a.Is = wsgu ? Is : 0;
+    a.renormalize = renorm;
+    a.nR = (E + kLayerWaves - 1) / kLayerWaves;
+    a.nS = a.Is / kLayerWaves;
+    a.nW13 = K * (I / kLayerWaves);
+    const int lpr = I >= 512 ? kWave : I / 8;
+    a.nW2 = H / ((kWave / lpr) * kLayerWaves);
+    a.logits = logits;
+    a.ids = ids;
+    a.weights = w;
+    a.act = act;
+    a.act_s = act_s;
+    a.y = (f16 *)y;
+    a.sync = sync;
+    switch (H / 512) {
+    case 2: return launch_layer_h<2>(a, s);
+    case 4: return launch_layer_h<4>(a, s);
+    case 8: return launch_layer_h<8>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_read_timeouts(const LayerSync *sync, unsigned *out, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_read_timeouts, dim3(1), dim3(kWave), 0, s, sync, out);
     return last();
 }
 

@@ -1,23 +1,30 @@
 """One decode layer's buffers and call sequence, and a hipGraph of many layers.
 
-A layer issues, on one stream: shared_expert (independent of routing, so it
-goes first), moe_route, moe_decode_fused (which adds the shared output before
-its single fp16 rounding).  A stack captures the sequence of every layer into
-one hipGraph (torch.cuda.CUDAGraph drives stream capture; the captured nodes
-are this library's kernels), so one replay is one host call.
+A layer runs either as moe_layer_decode (one fused launch where the sizes
+allow) or as the three entry points on one stream: shared_expert (independent
+of routing, so it goes first), moe_route, moe_decode_fused (which adds the
+shared output before its single fp16 rounding).  A stack captures every
+layer's launches into one hipGraph (torch.cuda.CUDAGraph drives stream
+capture; the captured nodes are this library's kernels), so one replay is one
+host call.
 """
 from __future__ import annotations
 
 import torch
 
-from .api import moe_decode_fused, moe_route, shared_expert, workspace
+from .api import moe_decode_fused, moe_layer_decode, moe_route, shared_expert, workspace
 from .synth import LayerShape
 
 
 class DecodeLayer:
-    """Weights, inputs and preallocated outputs of one layer (all on one device)."""
+    """Weights, inputs and preallocated outputs of one layer (all on one device).
 
-    def __init__(self, tensors: dict, shape: LayerShape):
+    forward() runs the layer through moe_layer_decode (one launch where the sizes
+    allow); forward_separate() issues the three entry points one after another.
+    """
+
+    def __init__(self, tensors: dict, shape: LayerShape, fused: bool = True):
+        self.fused = fused
         self.shape = shape
         self.t = tensors
         dev = tensors["x"].device
@@ -30,6 +37,15 @@ class DecodeLayer:
         self.ws = workspace(max(M, 1), H, E, I, K, Is, dev)
 
     def forward(self, stream=None):
+        if not self.fused:
+            return self.forward_separate(stream)
+        t, sh = self.t, self.shape
+        moe_layer_decode(t["x"], t["wr"], t["w13"], t["w2"], t["wsgu"], t["wsd"], sh.K,
+                         sh.renormalize, self.topk_ids, self.topk_w, self.logits, self.y, self.ws,
+                         stream=stream)
+        return self.y
+
+    def forward_separate(self, stream=None):
         t, sh = self.t, self.shape
         if self.s is not None:
             shared_expert(t["x"], t["wsgu"], t["wsd"], s_out=self.s, ws=self.ws, stream=stream)

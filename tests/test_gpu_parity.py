@@ -29,22 +29,26 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_layer(t, shape):
-    layer = DecodeLayer(t, shape)
+def run_layer(t, shape, fused=True):
+    layer = DecodeLayer(t, shape, fused=fused)
     layer.forward()
     torch.cuda.synchronize()
+    if fused:
+        assert moe.moe_dbg_layer_timeouts(layer.ws) == 0
     return layer
 
 
 def parity(shape, seed, tag=""):
+    """Both paths (three entry points; moe_layer_decode) against the oracle."""
     say("parity", tag, shape, "seed", seed)
     t = cases.draw_case(shape, seed, DEV)
-    layer = run_layer(t, shape)
     ref = cases.oracle_reference(t, shape, nthreads=8)
-    where = "%s seed %d" % (tag, seed)
-    cases.check_route(layer.topk_ids, layer.topk_w, layer.logits, ref, t, shape, where)
-    rel, mx = cases.check_y(layer.y, ref["y"], where)
-    say("  ok rel-L2 %.3g max-abs %.3g (x attempt %d)" % (rel, mx, t["attempt"]))
+    for fused in (False, True):
+        layer = run_layer(t, shape, fused)
+        where = "%s seed %d fused=%s" % (tag, seed, fused)
+        cases.check_route(layer.topk_ids, layer.topk_w, layer.logits, ref, t, shape, where)
+        rel, mx = cases.check_y(layer.y, ref["y"], where)
+        say("  ok fused=%s rel-L2 %.3g max-abs %.3g (x attempt %d)" % (fused, rel, mx, t["attempt"]))
     return t, layer, ref
 
 
@@ -238,7 +242,11 @@ def test_scaling_w2_doubles_output_bitwise():
     t2 = dict(t)
     t2["w2"] = t["w2"] * 2
     y2 = run_layer(t2, sh).y
-    assert torch.equal(y2, y1 * 2)
+    # the fp32 sum doubles exactly; rounding to fp16 commutes with doubling only for
+    # normal fp16 results (subnormals sit on a fixed 2^-24 grid)
+    normal = y1.float().abs() >= 2.0 ** -14
+    assert torch.equal(y2[normal], (y1 * 2)[normal])
+    assert torch.all((y2.float() - 2 * y1.float()).abs()[~normal] <= 2.0 ** -23)
 
 
 def test_graph_replay_equals_eager_bitwise():
