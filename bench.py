@@ -240,6 +240,60 @@ def summarize_trace(trace_dir, out_path, cmd):
     print("\n".join(lines))
 
 
+def probes(dev):
+    """Empty-kernel launch latency, hipGraph kernel-node gap, and the read
+    bandwidth of a 2 GiB stream (the practical HBM ceiling)."""
+    import torch
+    import routed_expert_gemv_amd as moe
+
+    res = {}
+    for _ in range(20):
+        moe.moe_probe_empty()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(200):
+        moe.moe_probe_empty()
+    b.record()
+    torch.cuda.synchronize()
+    res["empty_launch_us"] = round(a.elapsed_time(b) * 1e3 / 200, 3)
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_probe_empty()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(100):
+            moe.moe_probe_empty()
+    g.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    res["graph_node_us"] = round(a.elapsed_time(b) * 1e3 / 1000, 3)
+
+    buf = torch.zeros((2 << 30) // 2, dtype=torch.float16, device=dev)
+    out = torch.zeros(1, dtype=torch.float32, device=dev)
+    moe.moe_probe_read(buf, out)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        moe.moe_probe_read(buf, out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 10
+    res["read_2GiB_GBs"] = round(buf.numel() * 2 / (ms * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -251,6 +305,7 @@ def main():
                     help="fused: moe_layer_decode (one launch per layer); separate: the "
                          "three entry points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--counters-pass", action="store_true",
                     help="run the rocprofv3 --pmc workload (copy calibration + W13 launches)")
@@ -344,6 +399,11 @@ def main():
                      "avg_launch_us": round(k_us, 3), "bytes_per_launch": k_b},
         "cpu_baseline": None,
     }
+    if not args.no_probes:
+        del stack
+        out["probes"] = probes(dev)
+        log("probes: %s" % out["probes"])
+        out["frac_of_read_probe"] = round(gbs_expert / out["probes"]["read_2GiB_GBs"], 4)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on the host (~%.0f s)" % args.cpu_budget)
         out["cpu_baseline"] = cpu_baseline(tensors, sh, args.cpu_budget)

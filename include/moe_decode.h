@@ -134,34 +134,50 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
                             int M, int H, int E, int I, int K, void *y, void *ws, size_t ws_bytes,
                             hipStream_t stream);
 
-/* Steps 1-5, the whole layer: the same results, bit for bit, as
- *   shared_expert -> moe_route -> moe_decode_fused(shared_in = s)
- * on one stream, in as few launches as the sizes allow.  For M = 1,
- * H in {1024, 2048, 4096}, I <= 1024, Is in {0, I} and K*I <= 8192 it is ONE
- * kernel: workgroups take the router, shared gate/up, routed W13 and routed
- * W2 roles in that order and hand results on through counters in the
- * workspace (a workgroup only waits on lower-numbered ones; every wait is
- * bounded), so routed W2 rows are already streaming while W13 finishes.
- * Other sizes run the three calls' kernels in sequence.
+/* Steps 1-5, the whole layer, in as few launches as the sizes allow.
+ * Results equal the three-call sequence shared_expert, moe_route,
+ * moe_decode_fused bit for bit (routing outputs and y), whichever way it runs.
+ *
+ * For M = 1, H in {1024, 2048}, I <= 1024, Is in {0, I}, K*I <= 8192 and
+ * E <= 1024 it is ONE kernel: workgroups take the router, shared-expert
+ * gate/up, routed gate/up and down roles by index, and hand logits, the
+ * selection and the activations on through device memory; see
+ * moe_layer_fused.  Other sizes run the three calls' kernels in sequence.
  *   x, w_router, w13, w2  as for moe_route / moe_decode_fused
  *   w_gate_up, w_down     shared expert [2Is, H] / [H, Is], or both NULL (Is ignored)
  *   topk_ids, topk_w, logits  outputs as for moe_route
  *   y          [M, H] fp16 out
  *   ws         >= moe_workspace_bytes(M, H, E, I, K, Is) bytes, ZERO-FILLED before its
- *              first use with this function; every call leaves its synchronisation
- *              words at zero again.  Calls that share a ws must not overlap in time.
- * A wait that exhausts its poll budget (not expected on an idle GPU) is counted
- * in the workspace; moe_dbg_layer_timeouts reads the count. */
+ *              first use with this function; the kernel keeps a launch count and
+ *              synchronisation counters there between calls.  Calls that share a ws
+ *              must not overlap in time.
+ * Every wait between workgroups is bounded; a wait that exhausts its poll
+ * budget (not expected on an idle GPU) is counted in the workspace, see
+ * moe_dbg_layer_diag. */
 moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13, const void *w2,
                             const void *w_gate_up, const void *w_down, int M, int H, int E, int I,
                             int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
                             float *logits, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* 1 if moe_layer_decode runs as one kernel for these sizes on the current
+ * device, 0 if it runs the separate kernels (or the sizes are unsupported). */
+int moe_layer_fused(int M, int H, int E, int I, int K, int Is);
+
 /* ---- test-only probes (not part of the decode path) --------------------- */
 
-/* Number of bounded waits of moe_layer_decode that gave up, for workspace `ws`,
- * written to out[0] (device). */
-moe_status moe_dbg_layer_timeouts(const void *ws, unsigned *out, hipStream_t stream);
+/* An empty kernel: launch latency and the gap between hipGraph kernel nodes. */
+moe_status moe_probe_empty(hipStream_t stream);
+
+/* Streams `bytes` (a multiple of 16) of device memory at `src` with
+ * non-temporal 16-byte loads (8 in flight per thread): the achievable read
+ * bandwidth.  out: one device float, written only in a case that zero-filled
+ * input never produces. */
+moe_status moe_probe_read(const void *src, size_t bytes, float *out, hipStream_t stream);
+
+/* Diagnostics of moe_layer_decode on workspace `ws`, written to out[0..2)
+ * (device): out[0] = bounded waits that gave up since the workspace was
+ * zero-filled (0 when all went as designed), out[1] = 0 (reserved). */
+moe_status moe_dbg_layer_diag(const void *ws, unsigned *out, hipStream_t stream);
 
 /* Sums 64 fp32 values with one wavefront's cross-lane (DPP) reduction, the
  * same routine the GEMV kernels use; out[0] = the sum.  in: [64] device. */

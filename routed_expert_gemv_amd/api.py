@@ -249,10 +249,33 @@ def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int =
     return y, topk_ids, topk_w, logits
 
 
-def moe_dbg_layer_timeouts(ws, stream=None) -> int:
-    """Test probe: how many bounded waits of moe_layer_decode gave up on this workspace."""
+def moe_layer_fused(M: int, H: int, E: int, I: int, K: int, Is: int = 0) -> bool:
+    """Whether moe_layer_decode runs as one kernel for these sizes on the current device."""
+    return bool(_lib.lib().moe_layer_fused(M, H, E, I, K, Is))
+
+
+def moe_dbg_layer_diag(ws, stream=None) -> dict:
+    """Test probe: diagnostics moe_layer_decode keeps in the workspace."""
     _dev_tensor("ws", ws, torch.uint8)
-    out = torch.zeros(1, dtype=torch.int32, device=ws.device)
-    st = _lib.lib().moe_dbg_layer_timeouts(_ptr(ws), _ptr(out), _stream(stream, ws.device))
-    _check("moe_dbg_layer_timeouts", st)
-    return int(out.item())
+    out = torch.zeros(2, dtype=torch.int32, device=ws.device)
+    st = _lib.lib().moe_dbg_layer_diag(_ptr(ws), _ptr(out), _stream(stream, ws.device))
+    _check("moe_dbg_layer_diag", st)
+    v = out.tolist()
+    return {"timeouts": v[0]}
+
+
+def moe_probe_empty(stream=None):
+    """Bench probe: launch one empty kernel."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    _check("moe_probe_empty", _lib.lib().moe_probe_empty(_stream(stream, dev)))
+
+
+def moe_probe_read(buf, out=None, stream=None):
+    """Bench probe: stream the bytes of a device tensor with 16-byte loads."""
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    out = torch.zeros(1, dtype=torch.float32, device=buf.device) if out is None else out
+    n = buf.numel() * buf.element_size()
+    _check("moe_probe_read", _lib.lib().moe_probe_read(_ptr(buf), n - n % 16, _ptr(out),
+                                                       _stream(stream, buf.device)))
+    return out

@@ -22,6 +22,14 @@ size_t routed_ws_bytes(int M, int I, int K)
     return kRoutedActOffset + align256((size_t)M * K * I * sizeof(float));
 }
 
+// moe_layer_decode also needs the fused kernel's partial outputs, after the rest
+size_t layer_ws_bytes(int M, int H, int E, int I, int K, int Is)
+{
+    size_t n = routed_ws_bytes(M, I, K);
+    if (layer_fusable(M, H, E, I, K, Is)) n += align256(layer_partial_bytes(H, E, I, K, Is));
+    return n;
+}
+
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 } // namespace
@@ -46,7 +54,7 @@ const char *moe_status_str(moe_status s)
 size_t moe_workspace_bytes(int M, int H, int E, int I, int K, int Is)
 {
     if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (Is != 0 && !i_ok(Is))) return 0;
-    return routed_ws_bytes(M < 1 ? 1 : M, I, K);
+    return layer_ws_bytes(M < 1 ? 1 : M, H, E, I, K, Is);
 }
 
 moe_status moe_route(const void *x, const void *w_router, int M, int H, int E, int K,
@@ -110,14 +118,14 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
         !al(topk_w, 4) || !al(logits, 4) || !al(y, 2) || !al(ws, 256) ||
         (shared && (!al(w_gate_up, 16) || !al(w_down, 16))))
         return MOE_ERR_ALIGN;
-    if (ws_bytes < routed_ws_bytes(M, I, K)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < layer_ws_bytes(M, H, E, I, K, Is)) return MOE_ERR_WORKSPACE;
     char *base = static_cast<char *>(ws);
     float *act_s = reinterpret_cast<float *>(base);
     float *act = reinterpret_cast<float *>(base + kRoutedActOffset);
     if (layer_fusable(M, H, E, I, K, Is))
-        return hip_status(launch_layer(x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is,
-                                       renormalize, topk_ids, topk_w, logits, y, act, act_s,
-                                       reinterpret_cast<LayerSync *>(base + kSyncOffset), stream));
+        return hip_status(launch_layer(
+            x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is, renormalize, topk_ids, topk_w,
+            logits, y, base, reinterpret_cast<float *>(base + routed_ws_bytes(M, I, K)), stream));
     float *s_out = shared ? reinterpret_cast<float *>(base + kSharedOutOffset) : nullptr;
     hipError_t err = hipSuccess;
     if (shared) err = launch_shared(x, w_gate_up, w_down, M, H, Is, s_out, act_s, stream);
@@ -129,13 +137,26 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
     return hip_status(err);
 }
 
-moe_status moe_dbg_layer_timeouts(const void *ws, unsigned *out, hipStream_t stream)
+int moe_layer_fused(int M, int H, int E, int I, int K, int Is)
+{
+    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (Is != 0 && !i_ok(Is))) return 0;
+    return layer_fusable(M, H, E, I, K, Is) ? 1 : 0;
+}
+
+moe_status moe_dbg_layer_diag(const void *ws, unsigned *out, hipStream_t stream)
 {
     if (!ws || !out) return MOE_ERR_NULL;
     if (!al(ws, 256) || !al(out, 4)) return MOE_ERR_ALIGN;
-    const char *base = static_cast<const char *>(ws);
-    return hip_status(launch_read_timeouts(reinterpret_cast<const LayerSync *>(base + kSyncOffset),
-                                           out, stream));
+    return hip_status(launch_read_layer_diag(static_cast<const char *>(ws), out, stream));
+}
+
+moe_status moe_probe_empty(hipStream_t stream) { return hip_status(launch_probe_empty(stream)); }
+
+moe_status moe_probe_read(const void *src, size_t bytes, float *out, hipStream_t stream)
+{
+    if (!src || !out) return MOE_ERR_NULL;
+    if (!al(src, 16) || !al(out, 4) || bytes % 16) return MOE_ERR_ALIGN;
+    return hip_status(launch_probe_read(src, bytes, out, stream));
 }
 
 moe_status moe_dbg_wave_sum(const float *in, float *out, hipStream_t stream)

@@ -285,26 +285,17 @@ __device__ __forceinline__ void st_agent(float *p, float v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <bool COHERENT>
-__device__ __forceinline__ float ld_logit(const float *p)
-{
-    return COHERENT ? ld_agent(p) : *p;
-}
-
-// Top-K of the E <= 64*NPL logits L[0..E).  Lane k < K receives the k-th
+// Top-K of E <= 64*NPL logits held by the wave: v[i] is the logit of expert
+// i*64 + lane (ignored where that is >= E).  Lane k < K receives the k-th
 // selected expert id and its logit; returns the largest logit (wave-uniform).
-// COHERENT: L was written by other workgroups of the same launch.
-template <int NPL, bool COHERENT = false>
-__device__ __forceinline__ float wave_topk(const float *__restrict__ L, int E, int K, int &my_id,
-                                           float &my_l)
+template <int NPL>
+__device__ __forceinline__ float wave_topk_vals(const float (&v)[NPL], int E, int K, int &my_id,
+                                                float &my_l)
 {
     const int lane = lane_id();
     uint32_t key[NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = i * kWave + lane;
-        key[i] = e < E ? order_key(ld_logit<COHERENT>(L + e)) : 0u;
-    }
+    for (int i = 0; i < NPL; ++i) key[i] = i * kWave + lane < E ? order_key(v[i]) : 0u;
     float lmax = 0.0f;
     my_id = 0;
     my_l = 0.0f;
@@ -334,9 +325,9 @@ __device__ __forceinline__ float wave_topk(const float *__restrict__ L, int E, i
 
 // Routing weight of the slot held by this lane (valid in lanes < K): softmax
 // over the selected logits (renormalize) or over all E logits.
-template <bool COHERENT = false>
-__device__ __forceinline__ float topk_weight(const float *__restrict__ L, int E, int K,
-                                             int renormalize, float my_l, float lmax)
+template <int NPL>
+__device__ __forceinline__ float topk_weight_vals(const float (&v)[NPL], int E, int K,
+                                                  int renormalize, float my_l, float lmax)
 {
     const int lane = lane_id();
     const float ex = lane < K ? expf(my_l - lmax) : 0.0f;
@@ -345,7 +336,9 @@ __device__ __forceinline__ float topk_weight(const float *__restrict__ L, int E,
         z = wave_sum(ex);
     } else {
         float part = 0.0f;
-        for (int e = lane; e < E; e += kWave) part += expf(ld_logit<COHERENT>(L + e) - lmax);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i)
+            if (i * kWave + lane < E) part += expf(v[i] - lmax);
         z = wave_sum(part);
     }
     return ex / z;
@@ -359,10 +352,13 @@ __global__ __launch_bounds__(kWave) void k_topk(const float *__restrict__ logits
     const int m = blockIdx.x;
     const int lane = lane_id();
     const float *L = logits + (size_t)m * E;
+    float v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) v[i] = i * kWave + lane < E ? L[i * kWave + lane] : 0.0f;
     int my_id;
     float my_l;
-    const float lmax = wave_topk<NPL>(L, E, K, my_id, my_l);
-    const float w = topk_weight(L, E, K, renormalize, my_l, lmax);
+    const float lmax = wave_topk_vals<NPL>(v, E, K, my_id, my_l);
+    const float w = topk_weight_vals<NPL>(v, E, K, renormalize, my_l, lmax);
     if (lane < K) {
         ids[(size_t)m * K + lane] = my_id;
         weights[(size_t)m * K + lane] = w;
@@ -544,34 +540,44 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
 
 
 // ---------------------------------------------------------------- fused layer (M = 1)
-// The whole layer in one launch.  Workgroups of 16 waves take roles by block
-// index, in dependency order:
-//   [0, nR)            router: one wave per expert row -> logits
-//   [.., +nS)          shared expert gate/up + SiLU*mul -> act_s
-//   [.., +nW13)        routed W13 + SiLU*mul: waits for the router, selects the
-//                      experts itself (every wave runs the same top-k), -> act
-//   [.., +nW2)         routed W2 + combine + shared down: selects the experts,
-//                      issues its W2 (and shared down) row loads, then waits
-//                      for every W13 / shared gate-up block, stages the
-//                      activations in LDS and produces y.
-// A block only waits on blocks with lower indices.  Blocks are dispatched in
-// index order on each XCD, so the lowest unfinished block can always run:
-// the waits cannot deadlock whatever the occupancy.  Every wait is bounded
-// (kSpinLimit polls); a wait that gives up bumps sync->timeouts and goes on,
-// so every wave exits.  The last block to finish re-arms the counters for the
-// next launch (the workspace's sync words start at zero and end at zero).
-//
-// Hand-off without cache-wide fences: data read by other blocks (logits,
-// act, act_s) is stored and loaded with agent-scope coherent accesses; each
-// wave drains its stores (s_waitcnt) before the block barrier, after which
-// one thread bumps the counter.  A waiting block's thread 0 polls with
-// exponential back-off, then the block barrier releases its waves.
-//
-// Arithmetic per element is the same device code as the separate kernels, so
-// the results equal shared_expert + moe_route + moe_decode_fused bit for bit.
+// The whole layer in one launch.  Workgroups of 16 waves take roles by index:
+//   [0, nR)          router: one wave per two expert rows -> logits; the last
+//                    router workgroup (by arrival) selects the experts once
+//                    and publishes ids + weights, tagged, in kRouteCopies
+//                    copies (so the pollers spread over many lines)
+//   [.., +nS)        shared expert gate/up + SiLU*mul: one wave per row pair
+//                    -> tagged act_s
+//   [.., +nW13)      routed W13 + SiLU*mul: waits for the routing, one wave
+//                    per (expert, row pair) -> tagged act
+//   [.., +nW2)       routed W2 + combine + shared down: loads its shared-down
+//                    rows, waits for the routing, loads its W2 rows (up to 8
+//                    experts in flight), gathers the tagged activations into
+//                    LDS and writes y.
+// A hand-off between workgroups has to go through memory (on this GPU only
+// agent-coherent loads see another workgroup's stores) and anything waiting
+// for a store acknowledgement queues behind the weight stream.  So published
+// values are 64-bit agent-coherent stores of (epoch << 32 | value bits) and a
+// consumer checks every value's tag (the epoch is read at launch start; the
+// last workgroup to finish advances it).  Counters are only hints, bumped
+// without waiting for the stores, that tell a consumer when gathering is
+// likely to succeed at once; the tags decide.  The one exception is the
+// routing: router workgroups drain their logit stores before taking a ticket,
+// so the last ticket holder reads every logit.
+// A workgroup only waits on lower-numbered ones (dispatch is in index order
+// per XCD, so the lowest unfinished one can always run), and every wait is
+// bounded (kSpinLimit polls, counted in sync->timeouts when exhausted).
+// Arithmetic per element is the same device code as the separate kernels
+// (same lane mapping, same reduction trees, same order), so the results equal
+// shared_expert + moe_route + moe_decode_fused bit for bit.
 constexpr unsigned kSpinLimit = 1u << 17; // ~0.1 s of polling at most
-constexpr int kLayerWaves = 16;
-constexpr int kLayerBlock = kLayerWaves * kWave;
+constexpr int kLWaves = 16;
+constexpr int kLBlock = kLWaves * kWave;
+constexpr int kRouterRowsPerWave = 2;
+constexpr int kRouteCopies = 32;
+constexpr int kRouteWords = 2 * kMaxTopk; // ids then weights, tagged
+constexpr int kHints = 16;
+
+typedef unsigned long long u64;
 
 struct LayerArgs {
     const f16 *x, *wr, *w13, *w2, *wsgu, *wsd;
@@ -580,10 +586,12 @@ struct LayerArgs {
     float *logits;
     int32_t *ids;
     float *weights;
-    float *act;
-    float *act_s;
     f16 *y;
     LayerSync *sync;
+    float *logits_c;  // [E] logits for the selecting workgroup (agent-coherent)
+    u64 *t_route;     // [kRouteCopies][kRouteWords]
+    u64 *t_act;       // [K * I]
+    u64 *t_act_s;     // [Is]
 };
 
 __device__ __forceinline__ unsigned ld_relaxed(const unsigned *p)
@@ -591,82 +599,129 @@ __device__ __forceinline__ unsigned ld_relaxed(const unsigned *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// thread 0 polls until sum(counters[0..n)) >= target and other >= target2
-__device__ __forceinline__ void block_wait(const SyncWord *counters, int n, unsigned target,
-                                           const SyncWord *other, unsigned target2,
-                                           LayerSync *sync)
+__device__ __forceinline__ u64 ld_tag(const u64 *p)
 {
-    if (threadIdx.x == 0) {
-        unsigned it = 0, nap = 1;
-        for (; it < kSpinLimit; ++it) {
-            unsigned sum = 0;
-            for (int i = 0; i < n; ++i) sum += ld_relaxed(&counters[i].v);
-            if (sum >= target && (other == nullptr || ld_relaxed(&other->v) >= target2)) break;
-            if (nap == 1) __builtin_amdgcn_s_sleep(1);
-            else if (nap == 2) __builtin_amdgcn_s_sleep(2);
-            else __builtin_amdgcn_s_sleep(4);
-            nap = nap < 4 ? nap + 1 : nap;
-        }
-        if (it == kSpinLimit)
-            __hip_atomic_fetch_add(&sync->timeouts.v, 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// every wave's agent-coherent stores have completed; then count the block
-__device__ __forceinline__ void block_signal(SyncWord *counter)
+__device__ __forceinline__ void st_tag(u64 *p, unsigned ep, uint32_t bits)
 {
+    __hip_atomic_store(p, ((u64)ep << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void bump(unsigned *p)
+{
+    __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void nap(unsigned it)
+{
+    if (it < 2) __builtin_amdgcn_s_sleep(2);
+    else __builtin_amdgcn_s_sleep(8);
+}
+
+__device__ __forceinline__ int lwave() { return (int)(threadIdx.x / kWave); }
+
+__device__ __forceinline__ void count_timeout(LayerSync *sync) { bump(&sync->timeouts.v); }
+
+template <int HC, int NPL>
+__device__ __forceinline__ void role_router(const LayerArgs &a, int b, unsigned ep, int *sh_last)
+{
+    constexpr int H = 512 * HC;
+    const int e0 = (b * kLWaves + lwave()) * kRouterRowsPerWave;
+    if (e0 < a.E) {
+        f16x8 xv[HC], w0[HC], w1[HC];
+        load_x<HC>(a.x, xv);
+        load_row<HC>(a.wr + (size_t)e0 * H, w0);
+        const bool two = e0 + 1 < a.E;
+        if (two) load_row<HC>(a.wr + (size_t)(e0 + 1) * H, w1);
+        const float t0 = row_dot<HC>(w0, xv);
+        const float t1 = two ? row_dot<HC>(w1, xv) : 0.0f;
+        if (lane_id() == 0) {
+            st_agent(a.logits_c + e0, t0);
+            a.logits[e0] = t0;
+            if (two) {
+                st_agent(a.logits_c + e0 + 1, t1);
+                a.logits[e0 + 1] = t1;
+            }
+        }
+    }
+    // drain the logit stores, then take a ticket; the last ticket selects
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0)
-        __hip_atomic_fetch_add(&counter->v, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void block_finish(LayerSync *sync, unsigned total)
-{
+        *sh_last = __hip_atomic_fetch_add(&a.sync->router_done.v, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.nR - 1u;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = __hip_atomic_fetch_add(&sync->blocks_done.v, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (old == total - 1) {
-            // every block of this launch is past its waits: re-arm for the next one
-            __hip_atomic_store(&sync->router_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&sync->shared_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int i = 0; i < kW13Counters; ++i)
-                __hip_atomic_store(&sync->w13_done[i].v, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&sync->blocks_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    if (!*sh_last || lwave() != 0) return;
+    const int lane = lane_id();
+    float v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = i * kWave + lane;
+        v[i] = e < a.E ? ld_agent(a.logits_c + e) : 0.0f;
+    }
+    int my_id;
+    float my_l;
+    const float lmax = wave_topk_vals<NPL>(v, a.E, a.K, my_id, my_l);
+    const float my_w = topk_weight_vals<NPL>(v, a.E, a.K, a.renormalize, my_l, lmax);
+    if (lane < a.K) {
+        a.ids[lane] = my_id;
+        a.weights[lane] = my_w;
+    }
+    // kRouteCopies copies of [ids | weights], lanes 0..K-1 and 16..16+K-1 of each
+    for (int c = 0; c < kRouteCopies; c += 2) {
+        const int copy = c + lane / 32, slot = lane % 32;
+        const int k = slot % kMaxTopk;
+        const int idk = __shfl(my_id, k);
+        const float wk = __shfl(my_w, k);
+        if (k < a.K)
+            st_tag(a.t_route + (size_t)copy * kRouteWords + slot, ep,
+                   slot < kMaxTopk ? (uint32_t)idk : __builtin_bit_cast(uint32_t, wk));
     }
 }
 
-__device__ __forceinline__ int layer_wave() { return (int)(threadIdx.x / kWave); }
-
-// agent-coherent 16-byte load (data published by another block of this launch)
-__device__ __forceinline__ f32x4 ld_agent4(const float *p)
+template <int HC>
+__device__ __forceinline__ void role_shared_gate_up(const LayerArgs &a, int b, unsigned ep)
 {
-    f32x4 v;
-    asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
-                 : "=v"(v)
-                 : "v"(p)
-                 : "memory");
-    return v;
+    constexpr int H = 512 * HC;
+    const int j = b * kLWaves + lwave();
+    f16x8 xv[HC], wg[HC], wu[HC];
+    load_x<HC>(a.x, xv);
+    load_row<HC>(a.wsgu + (size_t)j * H, wg);
+    load_row<HC>(a.wsgu + (size_t)(a.Is + j) * H, wu);
+    const float g = row_dot<HC>(wg, xv);
+    const float up = row_dot<HC>(wu, xv);
+    if (lane_id() == 0) st_tag(a.t_act_s + j, ep, __builtin_bit_cast(uint32_t, silu_mul(g, up)));
+    __syncthreads();
+    if (threadIdx.x == 0) bump(&a.sync->shared_hint.v);
 }
 
-// Routing for the whole block: wave 0 reads the published logits and selects;
-// lane k of every wave then holds the k-th expert id and weight.
-template <int NPL>
-__device__ __forceinline__ void block_route(const LayerArgs &a, int *sh_ids, float *sh_w,
-                                            int &my_id, float &my_w)
+// Wave 0 polls this workgroup's copy of the published routing until every
+// entry carries `ep`; lane k of every wave then holds expert k's id and weight.
+__device__ __forceinline__ void block_route(const LayerArgs &a, int b, unsigned ep, int *sh_ids,
+                                            float *sh_w, int &my_id, float &my_w)
 {
-    if (layer_wave() == 0) {
-        float my_l;
-        const float lmax = wave_topk<NPL, true>(a.logits, a.E, a.K, my_id, my_l);
-        my_w = topk_weight<true>(a.logits, a.E, a.K, a.renormalize, my_l, lmax);
-        if (lane_id() < a.K) {
-            sh_ids[lane_id()] = my_id;
-            sh_w[lane_id()] = my_w;
+    if (lwave() == 0) {
+        const int lane = lane_id();
+        const int k = lane % kMaxTopk;
+        const bool mine = lane < kRouteWords && k < a.K;
+        const u64 *src = a.t_route + (size_t)(b % kRouteCopies) * kRouteWords + lane;
+        u64 t = 0;
+        unsigned it = 0;
+        for (; it < kSpinLimit; ++it) {
+            bool ok = true;
+            if (mine) {
+                t = ld_tag(src);
+                ok = (unsigned)(t >> 32) == ep;
+            }
+            if (__ballot(!ok) == 0ull) break;
+            nap(it);
+        }
+        if (it == kSpinLimit && lane == 0) count_timeout(a.sync);
+        if (mine) {
+            if (lane < kMaxTopk) sh_ids[k] = (int)(uint32_t)t;
+            else sh_w[k] = __builtin_bit_cast(float, (uint32_t)t);
         }
     }
     __syncthreads();
@@ -676,48 +731,18 @@ __device__ __forceinline__ void block_route(const LayerArgs &a, int *sh_ids, flo
 }
 
 template <int HC>
-__device__ __forceinline__ void role_router(const LayerArgs &a, int b)
+__device__ __forceinline__ void role_w13(const LayerArgs &a, int b, unsigned ep, int *sh_ids,
+                                         float *sh_w)
 {
     constexpr int H = 512 * HC;
-    const int e = b * kLayerWaves + layer_wave();
-    if (e < a.E) {
-        f16x8 w[HC], xv[HC];
-        load_x<HC>(a.x, xv);
-        load_row<HC>(a.wr + (size_t)e * H, w);
-        const float t = row_dot<HC>(w, xv);
-        if (lane_id() == 0) st_agent(a.logits + e, t);
-    }
-    block_signal(&a.sync->router_done);
-}
-
-template <int HC>
-__device__ __forceinline__ void role_shared_gate_up(const LayerArgs &a, int b)
-{
-    constexpr int H = 512 * HC;
-    const int j = b * kLayerWaves + layer_wave();
-    f16x8 xv[HC], wg[HC], wu[HC];
-    load_x<HC>(a.x, xv);
-    load_row<HC>(a.wsgu + (size_t)j * H, wg);
-    load_row<HC>(a.wsgu + (size_t)(a.Is + j) * H, wu);
-    const float g = row_dot<HC>(wg, xv);
-    const float up = row_dot<HC>(wu, xv);
-    if (lane_id() == 0) st_agent(a.act_s + j, silu_mul(g, up));
-    block_signal(&a.sync->shared_done);
-}
-
-template <int HC, int NPL>
-__device__ __forceinline__ void role_w13(const LayerArgs &a, int b, int *sh_ids, float *sh_w)
-{
-    constexpr int H = 512 * HC;
-    const int per_expert = a.I / kLayerWaves;
+    const int per_expert = a.I / kLWaves;
     const int u = b / per_expert;
-    const int j = (b % per_expert) * kLayerWaves + layer_wave();
+    const int j = (b % per_expert) * kLWaves + lwave();
     f16x8 xv[HC];
     load_x<HC>(a.x, xv);
-    block_wait(&a.sync->router_done, 1, (unsigned)a.nR, nullptr, 0u, a.sync);
     int my_id;
     float my_w;
-    block_route<NPL>(a, sh_ids, sh_w, my_id, my_w);
+    block_route(a, b, ep, sh_ids, sh_w, my_id, my_w);
     const int expert = __builtin_amdgcn_readlane(my_id, u);
     const f16 *base = a.w13 + (size_t)expert * 2 * a.I * H;
     f16x8 wg[HC], wu[HC];
@@ -725,22 +750,67 @@ __device__ __forceinline__ void role_w13(const LayerArgs &a, int b, int *sh_ids,
     load_row<HC>(base + (size_t)(a.I + j) * H, wu);
     const float g = row_dot<HC>(wg, xv);
     const float up = row_dot<HC>(wu, xv);
-    if (lane_id() == 0) st_agent(a.act + (size_t)u * a.I + j, silu_mul(g, up));
-    block_signal(&a.sync->w13_done[b % kW13Counters]);
+    if (lane_id() == 0)
+        st_tag(a.t_act + (size_t)u * a.I + j, ep, __builtin_bit_cast(uint32_t, silu_mul(g, up)));
+    __syncthreads();
+    if (threadIdx.x == 0) bump(&a.sync->w13_hint[b % kHints].v);
 }
 
-template <int LPR, int CPL, int NPL>
-__device__ __forceinline__ void role_w2(const LayerArgs &a, int b, float *lds, int *sh_ids,
-                                        float *sh_w)
+// thread 0 polls the hint counters until the producers have (probably) published
+__device__ __forceinline__ void block_hint_wait(const LayerArgs &a)
+{
+    if (threadIdx.x == 0) {
+        unsigned it = 0;
+        for (; it < kSpinLimit; ++it) {
+            unsigned n = 0;
+            for (int i = 0; i < kHints; ++i) n += ld_relaxed(&a.sync->w13_hint[i].v);
+            if (n >= (unsigned)a.nW13 && ld_relaxed(&a.sync->shared_hint.v) >= (unsigned)a.nS) break;
+            nap(it);
+        }
+        if (it == kSpinLimit) count_timeout(a.sync);
+    }
+    __syncthreads();
+}
+
+// all threads gather the n tagged values src[0..n) into lds[0..n) until every
+// one carries `ep` (each thread re-reads only its own missing entries)
+__device__ __forceinline__ void block_gather(const u64 *src, int n, float *lds, unsigned ep,
+                                             LayerSync *sync)
+{
+    constexpr int kPer = 8; // entries per thread tracked in a bit mask (n <= 8 * kLBlock)
+    unsigned missing = 0;
+    for (int q = 0; q < kPer; ++q)
+        if ((int)threadIdx.x + q * kLBlock < n) missing |= 1u << q;
+    unsigned it = 0;
+    for (; it < kSpinLimit; ++it) {
+        for (int q = 0; q < kPer; ++q)
+            if (missing & (1u << q)) {
+                const int i = threadIdx.x + q * kLBlock;
+                const u64 t = ld_tag(src + i);
+                if ((unsigned)(t >> 32) == ep) {
+                    lds[i] = __builtin_bit_cast(float, (uint32_t)t);
+                    missing &= ~(1u << q);
+                }
+            }
+        if (__syncthreads_count(missing != 0) == 0) break;
+        nap(it);
+    }
+    if (it == kSpinLimit && threadIdx.x == 0) count_timeout(sync);
+    __syncthreads();
+}
+
+template <int LPR, int CPL>
+__device__ __forceinline__ void role_w2(const LayerArgs &a, int b, unsigned ep, float *lds,
+                                        int *sh_ids, float *sh_w)
 {
     constexpr int RPL = kWave / LPR;
     constexpr int BATCH = 8;
-    const int H = a.nW2 * kLayerWaves * RPL;
+    const int H = a.nW2 * kLWaves * RPL;
     const int lane = lane_id();
-    const int wave = layer_wave();
+    const int wave = lwave();
     const int r = lane / LPR;
     const int cl = lane % LPR;
-    const int h = (b * kLayerWaves + wave) * RPL + r;
+    const int h = (b * kLWaves + wave) * RPL + r;
     const bool shared = a.nS > 0;
 
     // shared down rows do not depend on routing: load them first
@@ -750,15 +820,10 @@ __device__ __forceinline__ void role_w2(const LayerArgs &a, int b, float *lds, i
 #pragma unroll
         for (int c = 0; c < CPL; ++c) ws[c] = stream_load(row + c * LPR + cl);
     }
-    block_wait(&a.sync->router_done, 1, (unsigned)a.nR, nullptr, 0u, a.sync);
     int my_id;
     float my_w;
-    block_route<NPL>(a, sh_ids, sh_w, my_id, my_w);
-    if (b == 0 && wave == 0 && lane < a.K) {
-        a.ids[lane] = my_id;
-        a.weights[lane] = my_w;
-    }
-    // first batch of routed W2 rows in flight before the wait for the activations
+    block_route(a, b, ep, sh_ids, sh_w, my_id, my_w);
+    // first batch of routed W2 rows in flight before the activations are gathered
     f16x8 wv[BATCH][CPL];
     const int first = a.K < BATCH ? a.K : BATCH;
 #pragma unroll
@@ -769,16 +834,10 @@ __device__ __forceinline__ void role_w2(const LayerArgs &a, int b, float *lds, i
 #pragma unroll
             for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
         }
-    block_wait(a.sync->w13_done, kW13Counters, (unsigned)a.nW13, shared ? &a.sync->shared_done : nullptr,
-               (unsigned)a.nS, a.sync);
-    // stage act [K, I] and act_s [Is] in LDS
+    block_hint_wait(a);
     const int n_act = a.K * a.I;
-    for (int i = threadIdx.x * 4; i < n_act; i += kLayerBlock * 4)
-        *reinterpret_cast<f32x4 *>(lds + i) = ld_agent4(a.act + i);
-    if (shared)
-        for (int i = threadIdx.x * 4; i < a.Is; i += kLayerBlock * 4)
-            *reinterpret_cast<f32x4 *>(lds + n_act + i) = ld_agent4(a.act_s + i);
-    __syncthreads();
+    block_gather(a.t_act, n_act, lds, ep, a.sync);
+    if (shared) block_gather(a.t_act_s, a.Is, lds + n_act, ep, a.sync);
 
     float acc = 0.0f;
     for (int u0 = 0; u0 < a.K; u0 += BATCH) {
@@ -827,27 +886,51 @@ __device__ __forceinline__ void role_w2(const LayerArgs &a, int b, float *lds, i
 }
 
 template <int HC, int LPR, int CPL, int NPL>
-__global__ __launch_bounds__(kLayerBlock) void k_layer(LayerArgs a)
+__global__ __launch_bounds__(kLBlock, 8) void k_layer(LayerArgs a)
 {
     extern __shared__ float lds[];
     __shared__ int sh_ids[kMaxTopk];
     __shared__ float sh_w[kMaxTopk];
+    __shared__ unsigned sh_ep;
+    __shared__ int sh_last;
     const int b = blockIdx.x;
-    const int total = a.nR + a.nS + a.nW13 + a.nW2;
+    if (threadIdx.x == 0) sh_ep = ld_relaxed(&a.sync->epoch.v) + 1u;
+    __syncthreads();
+    const unsigned ep = sh_ep;
     if (b < a.nR)
-        role_router<HC>(a, b);
+        role_router<HC, NPL>(a, b, ep, &sh_last);
     else if (b < a.nR + a.nS)
-        role_shared_gate_up<HC>(a, b - a.nR);
+        role_shared_gate_up<HC>(a, b - a.nR, ep);
     else if (b < a.nR + a.nS + a.nW13)
-        role_w13<HC, NPL>(a, b - a.nR - a.nS, sh_ids, sh_w);
+        role_w13<HC>(a, b - a.nR - a.nS, ep, sh_ids, sh_w);
     else
-        role_w2<LPR, CPL, NPL>(a, b - a.nR - a.nS - a.nW13, lds, sh_ids, sh_w);
-    block_finish(a.sync, (unsigned)total);
+        role_w2<LPR, CPL>(a, b - a.nR - a.nS - a.nW13, ep, lds, sh_ids, sh_w);
+
+    // the last workgroup of the launch re-arms the counters and advances the epoch
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned total = (unsigned)(a.nR + a.nS + a.nW13 + a.nW2);
+        const unsigned old = __hip_atomic_fetch_add(&a.sync->blocks_done.v, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        if (old == total - 1) {
+            __hip_atomic_store(&a.sync->router_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.sync->shared_hint.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < kHints; ++i)
+                __hip_atomic_store(&a.sync->w13_hint[i].v, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.sync->blocks_done.v, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.sync->epoch.v, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
 }
 
-__global__ void k_read_timeouts(const LayerSync *__restrict__ sync, unsigned *__restrict__ out)
+__global__ void k_read_layer_diag(const LayerSync *__restrict__ sync, unsigned *__restrict__ out)
 {
-    if (threadIdx.x == 0) out[0] = ld_relaxed(&sync->timeouts.v);
+    if (threadIdx.x == 0) {
+        out[0] = ld_relaxed(&sync->timeouts.v);
+        out[1] = 0u;
+    }
 }
 
 // ---------------------------------------------------------------- group table only
@@ -861,6 +944,27 @@ __global__ __launch_bounds__(kWave) void k_group_table(const int32_t *__restrict
 }
 
 // ---------------------------------------------------------------- probes
+// empty kernel (launch latency and graph node gap)
+__global__ void k_probe_empty() {}
+
+// stream `n16` 16-byte chunks with non-temporal loads, 8 per thread in flight
+__global__ __launch_bounds__(256) void k_probe_read(const f16x8 *__restrict__ src, size_t n16,
+                                                    float *__restrict__ out)
+{
+    constexpr int L = 8;
+    const size_t base = (size_t)blockIdx.x * blockDim.x * L + threadIdx.x;
+    f16x8 v[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const size_t idx = base + (size_t)i * blockDim.x;
+        v[i] = idx < n16 ? stream_load(src + idx) : f16x8{};
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) acc += (float)v[i][0];
+    if (acc == 1.25e-3f) out[0] = acc; // keeps the loads; never true for zero-filled input
+}
+
 __global__ __launch_bounds__(kWave) void k_dbg_wave_sum(const float *__restrict__ in,
                                                          float *__restrict__ out)
 {
@@ -1026,6 +1130,21 @@ hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids
     return launch_w2<false>(act, w2, ids, tw, shared_in, M, H, I, K, table, y, s);
 }
 
+hipError_t launch_probe_empty(hipStream_t s)
+{
+    hipLaunchKernelGGL(k_probe_empty, dim3(1), dim3(kWave), 0, s);
+    return last();
+}
+
+hipError_t launch_probe_read(const void *src, size_t bytes, float *out, hipStream_t s)
+{
+    const size_t n16 = bytes / 16;
+    const size_t per_block = 256 * 8;
+    const unsigned blocks = (unsigned)((n16 + per_block - 1) / per_block);
+    hipLaunchKernelGGL(k_probe_read, dim3(blocks), dim3(256), 0, s, (const f16x8 *)src, n16, out);
+    return last();
+}
+
 hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s)
 {
     hipLaunchKernelGGL(k_dbg_wave_sum, dim3(1), dim3(kWave), 0, s, in, out);
@@ -1036,8 +1155,9 @@ hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s)
 // ---------------------------------------------------------------- fused layer launcher
 bool layer_fusable(int M, int H, int E, int I, int K, int Is)
 {
-    return M == 1 && (H == 1024 || H == 2048 || H == 4096) && I <= 1024 &&
-           (Is == 0 || Is == I) && K * I <= kFusedMaxAct;
+    // block_gather tracks at most 8 entries per thread: K*I and Is <= 8 * kLBlock
+    return M == 1 && (H == 1024 || H == 2048) && I <= 1024 && (Is == 0 || Is == I) &&
+           K * I <= 8 * kLBlock && K * I + Is <= kFusedMaxAct && E <= kMaxExperts;
 }
 
 template <int HC, int LPR, int CPL>
@@ -1046,12 +1166,12 @@ static hipError_t launch_layer_t(const LayerArgs &a, hipStream_t s)
     const int blocks = a.nR + a.nS + a.nW13 + a.nW2;
     const size_t lds = (size_t)(a.K * a.I + a.Is) * sizeof(float);
     if (a.E <= kWave)
-        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, 1>), dim3(blocks), dim3(kLayerBlock), lds, s, a);
+        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, 1>), dim3(blocks), dim3(kLBlock), lds, s, a);
     else if (a.E <= 4 * kWave)
-        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, 4>), dim3(blocks), dim3(kLayerBlock), lds, s, a);
+        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, 4>), dim3(blocks), dim3(kLBlock), lds, s, a);
     else
         hipLaunchKernelGGL((k_layer<HC, LPR, CPL, kMaxExperts / kWave>), dim3(blocks),
-                           dim3(kLayerBlock), lds, s, a);
+                           dim3(kLBlock), lds, s, a);
     return last();
 }
 
@@ -1068,10 +1188,18 @@ static hipError_t launch_layer_h(const LayerArgs &a, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
+size_t layer_partial_bytes(int, int E, int I, int K, int Is)
+{
+    // logits, tagged routing copies, tagged routed and shared activations
+    return align256((size_t)E * sizeof(float)) +
+           align256((size_t)kRouteCopies * kRouteWords * sizeof(u64)) +
+           align256((size_t)K * I * sizeof(u64)) + align256((size_t)Is * sizeof(u64));
+}
+
 hipError_t launch_layer(const void *x, const void *wr, const void *w13, const void *w2,
                         const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
-                        int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
-                        float *act_s, LayerSync *sync, hipStream_t s)
+                        int renorm, int32_t *ids, float *w, float *logits, void *y, char *ws,
+                        float *partial, hipStream_t s)
 {
     LayerArgs a;
     a.x = (const f16 *)x;
@@ -1085,29 +1213,35 @@ hipError_t launch_layer(const void *x, const void *wr, const void *w13, const vo
     a.K = K;
     a.Is = wsgu ? Is : 0;
     a.renormalize = renorm;
-    a.nR = (E + kLayerWaves - 1) / kLayerWaves;
-    a.nS = a.Is / kLayerWaves;
-    a.nW13 = K * (I / kLayerWaves);
+    a.nR = (E + kLWaves * kRouterRowsPerWave - 1) / (kLWaves * kRouterRowsPerWave);
+    a.nS = a.Is / kLWaves;
+    a.nW13 = K * (I / kLWaves);
     const int lpr = I >= 512 ? kWave : I / 8;
-    a.nW2 = H / ((kWave / lpr) * kLayerWaves);
+    a.nW2 = H / ((kWave / lpr) * kLWaves);
     a.logits = logits;
     a.ids = ids;
     a.weights = w;
-    a.act = act;
-    a.act_s = act_s;
     a.y = (f16 *)y;
-    a.sync = sync;
+    a.sync = reinterpret_cast<LayerSync *>(ws + kSyncOffset);
+    char *t = reinterpret_cast<char *>(partial);
+    a.logits_c = reinterpret_cast<float *>(t);
+    t += align256((size_t)E * sizeof(float));
+    a.t_route = reinterpret_cast<u64 *>(t);
+    t += align256((size_t)kRouteCopies * kRouteWords * sizeof(u64));
+    a.t_act = reinterpret_cast<u64 *>(t);
+    t += align256((size_t)K * I * sizeof(u64));
+    a.t_act_s = reinterpret_cast<u64 *>(t);
     switch (H / 512) {
     case 2: return launch_layer_h<2>(a, s);
     case 4: return launch_layer_h<4>(a, s);
-    case 8: return launch_layer_h<8>(a, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_read_timeouts(const LayerSync *sync, unsigned *out, hipStream_t s)
+hipError_t launch_read_layer_diag(const char *ws, unsigned *out, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_read_timeouts, dim3(1), dim3(kWave), 0, s, sync, out);
+    hipLaunchKernelGGL(k_read_layer_diag, dim3(1), dim3(kWave), 0, s,
+                       reinterpret_cast<const LayerSync *>(ws + kSyncOffset), out);
     return last();
 }
 

@@ -34,7 +34,7 @@ def run_layer(t, shape, fused=True):
     layer.forward()
     torch.cuda.synchronize()
     if fused:
-        assert moe.moe_dbg_layer_timeouts(layer.ws) == 0
+        assert moe.moe_dbg_layer_diag(layer.ws) == {"timeouts": 0}
     return layer
 
 
