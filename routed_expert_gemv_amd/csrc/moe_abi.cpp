@@ -122,6 +122,10 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
     char *base = static_cast<char *>(ws);
     float *act_s = reinterpret_cast<float *>(base);
     float *act = reinterpret_cast<float *>(base + kRoutedActOffset);
+    if (lean_ok(M, H, E, I, K, Is))
+        return hip_status(launch_lean(x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is,
+                                      renormalize, topk_ids, topk_w, logits, y, act, act_s,
+                                      reinterpret_cast<float *>(base + kSharedOutOffset), stream));
     if (layer_fusable(M, H, E, I, K, Is))
         return hip_status(launch_layer(
             x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is, renormalize, topk_ids, topk_w,

@@ -75,6 +75,11 @@ hipError_t launch_layer(const void *x, const void *wr, const void *w13, const vo
                         int renorm, int32_t *ids, float *w, float *logits, void *y, char *ws,
                         float *partial, hipStream_t s);
 hipError_t launch_read_layer_diag(const char *ws, unsigned *out, hipStream_t s);
+bool lean_ok(int M, int H, int E, int I, int K, int Is);
+hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
+                       const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
+                       int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
+                       float *act_s, float *s_out, hipStream_t s);
 hipError_t launch_probe_empty(hipStream_t s);
 hipError_t launch_probe_read(const void *src, size_t bytes, float *out, hipStream_t s);
 hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s);

@@ -285,38 +285,73 @@ __device__ __forceinline__ void st_agent(float *p, float v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ int wave_min_i32(int v)
+{
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, 0x142, 0xA, 0xF, false));
+    v = min(v, __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, 0x143, 0xC, 0xF, false));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Top-K of E <= 64*NPL logits held by the wave: v[i] is the logit of expert
 // i*64 + lane (ignored where that is >= E).  Lane k < K receives the k-th
 // selected expert id and its logit; returns the largest logit (wave-uniform).
+// Each lane first sorts its NPL (key, id) pairs by descending key, stably, so
+// equal keys keep ascending ids; then every round takes the largest head key
+// over the wave, the lowest id among the heads holding it (a second reduction
+// only when several lanes tie), and that lane pops its head.
 template <int NPL>
 __device__ __forceinline__ float wave_topk_vals(const float (&v)[NPL], int E, int K, int &my_id,
                                                 float &my_l)
 {
     const int lane = lane_id();
     uint32_t key[NPL];
+    int id[NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) key[i] = i * kWave + lane < E ? order_key(v[i]) : 0u;
+    for (int i = 0; i < NPL; ++i) {
+        id[i] = i * kWave + lane;
+        key[i] = id[i] < E ? order_key(v[i]) : 0u;
+    }
+    // odd-even transposition sort, swapping only strictly smaller keys upward (stable)
+#pragma unroll
+    for (int r = 0; r < NPL; ++r)
+#pragma unroll
+        for (int i = r & 1; i + 1 < NPL; i += 2)
+            if (key[i] < key[i + 1]) {
+                const uint32_t tk = key[i];
+                key[i] = key[i + 1];
+                key[i + 1] = tk;
+                const int ti = id[i];
+                id[i] = id[i + 1];
+                id[i + 1] = ti;
+            }
     float lmax = 0.0f;
     my_id = 0;
     my_l = 0.0f;
     for (int k = 0; k < K; ++k) {
-        uint32_t m = 0u;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) m = umax(m, key[i]);
-        m = wave_max_u32(m);
-        int id = -1;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i) {
-            const uint64_t b = __ballot(key[i] == m);
-            if (id < 0 && b != 0ull) id = i * kWave + __builtin_ctzll(b);
+        const uint32_t m = wave_max_u32(key[0]);
+        const uint64_t b = __ballot(key[0] == m);
+        int winner = __builtin_ctzll(b);
+        int wid = __builtin_amdgcn_readlane(id[0], winner);
+        if (__builtin_popcountll(b) > 1) { // equal keys in several lanes: lowest id first
+            wid = wave_min_i32(key[0] == m ? id[0] : 0x7FFFFFFF);
+            winner = __builtin_ctzll(__ballot(key[0] == m && id[0] == wid));
         }
+        if (lane == winner) {
 #pragma unroll
-        for (int i = 0; i < NPL; ++i)
-            if (i * kWave + lane == id) key[i] = 0u;
+            for (int i = 0; i + 1 < NPL; ++i) {
+                key[i] = key[i + 1];
+                id[i] = id[i + 1];
+            }
+            key[NPL - 1] = 0u;
+        }
         const float lv = key_value(m);
         if (k == 0) lmax = lv;
         if (lane == k) {
-            my_id = id;
+            my_id = wid;
             my_l = lv;
         }
     }
@@ -772,23 +807,39 @@ __device__ __forceinline__ void block_hint_wait(const LayerArgs &a)
     __syncthreads();
 }
 
+// Buffer resource over `bytes` bytes at `p` (raw addressing; loads past the end
+// return 0 instead of touching memory).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+// Cache policy of the relaxed agent-scope loads above (sc1), as a buffer-load
+// argument: the same agent-coherent read.
+constexpr int kAuxAgent = 16;
+
 // all threads gather the n tagged values src[0..n) into lds[0..n) until every
-// one carries `ep` (each thread re-reads only its own missing entries)
+// one carries `ep` (each thread re-reads only its own missing entries).  Entry
+// i = threadIdx.x + q * kLBlock: one per-thread offset, the q part is scalar,
+// so the poll holds no per-entry addresses in vector registers.
 __device__ __forceinline__ void block_gather(const u64 *src, int n, float *lds, unsigned ep,
                                              LayerSync *sync)
 {
     constexpr int kPer = 8; // entries per thread tracked in a bit mask (n <= 8 * kLBlock)
+    const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(src, n * (int)sizeof(u64));
+    const int voff = (int)threadIdx.x * (int)sizeof(u64);
     unsigned missing = 0;
     for (int q = 0; q < kPer; ++q)
         if ((int)threadIdx.x + q * kLBlock < n) missing |= 1u << q;
     unsigned it = 0;
     for (; it < kSpinLimit; ++it) {
+#pragma unroll
         for (int q = 0; q < kPer; ++q)
             if (missing & (1u << q)) {
-                const int i = threadIdx.x + q * kLBlock;
-                const u64 t = ld_tag(src + i);
-                if ((unsigned)(t >> 32) == ep) {
-                    lds[i] = __builtin_bit_cast(float, (uint32_t)t);
+                const auto t = __builtin_amdgcn_raw_buffer_load_b64(
+                    rsrc, voff, q * kLBlock * (int)sizeof(u64), kAuxAgent);
+                if (t[1] == ep) {
+                    lds[threadIdx.x + q * kLBlock] = __builtin_bit_cast(float, t[0]);
                     missing &= ~(1u << q);
                 }
             }
@@ -804,7 +855,7 @@ __device__ __forceinline__ void role_w2(const LayerArgs &a, int b, unsigned ep, 
                                         int *sh_ids, float *sh_w)
 {
     constexpr int RPL = kWave / LPR;
-    constexpr int BATCH = 8;
+    constexpr int BATCH = 8 / CPL; // W2 chunks in flight per lane: 8 (registers)
     const int H = a.nW2 * kLWaves * RPL;
     const int lane = lane_id();
     const int wave = lwave();
@@ -931,6 +982,202 @@ __global__ void k_read_layer_diag(const LayerSync *__restrict__ sync, unsigned *
         out[0] = ld_relaxed(&sync->timeouts.v);
         out[1] = 0u;
     }
+}
+
+// ---------------------------------------------------------------- layer path (M = 1)
+// Three launches for a whole layer at M = 1, plain grids of independent
+// workgroups (the kernel boundaries are the only hand-offs):
+//   k_router_shared  router rows -> logits; shared gate/up rows -> SiLU*mul
+//                    activations (routing-independent bytes that stream in the
+//                    router's latency shadow)
+//   k_expand         each routed workgroup selects the experts from the logits
+//                    itself, then its gate/up rows of the selected expert ->
+//                    activations; the shared down rows -> s (fp32)
+//   k_reduce         routed down rows with the weighted combine, + s, the one
+//                    fp16 rounding
+// The per-element arithmetic is the separate kernels' (the same device
+// functions, lane mappings and reduction trees, in the same order), so the
+// results equal shared_expert + moe_route + moe_decode_fused bit for bit.
+
+// gate row j and up row I + j of the expert at `base` -> silu(gate) * up
+// (the W13 kernel's arithmetic for one token)
+template <int HC>
+__device__ __forceinline__ float w13_pair(const f16 *__restrict__ x, const f16 *__restrict__ base,
+                                          int I, int j)
+{
+    constexpr int H = 512 * HC;
+    f16x8 xv[HC], wg[HC], wu[HC];
+    load_x<HC>(x, xv);
+    const f16x8 *grow = reinterpret_cast<const f16x8 *>(base + (size_t)j * H);
+    const f16x8 *urow = reinterpret_cast<const f16x8 *>(base + (size_t)(I + j) * H);
+#pragma unroll
+    for (int c = 0; c < HC; ++c) {
+        wg[c] = stream_load(grow + c * kWave + lane_id());
+        wu[c] = stream_load(urow + c * kWave + lane_id());
+    }
+    const float g = row_dot<HC>(wg, xv);
+    const float up = row_dot<HC>(wu, xv);
+    return silu_mul(g, up);
+}
+
+// Workgroups [0, ceil(E/4)): one wave per router row (the router kernel's
+// arithmetic); the rest: one wave per shared gate/up row pair.
+template <int HC>
+__global__ __launch_bounds__(kBlock) void k_router_shared(const f16 *__restrict__ x,
+                                                          const f16 *__restrict__ wr,
+                                                          const f16 *__restrict__ wsgu, int E,
+                                                          int Is, float *__restrict__ logits,
+                                                          float *__restrict__ act_s)
+{
+    constexpr int H = 512 * HC;
+    const int wave = threadIdx.x / kWave;
+    const int router_blocks = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+    if ((int)blockIdx.x < router_blocks) {
+        const int e = blockIdx.x * kWavesPerBlock + wave;
+        if (e >= E) return;
+        f16x8 w[HC], xv[HC];
+        load_row<HC>(wr + (size_t)e * H, w);
+        load_x<HC>(x, xv);
+        const float t = row_dot<HC>(w, xv);
+        if (lane_id() == 0) logits[e] = t;
+    } else {
+        const int j = (blockIdx.x - router_blocks) * kWavesPerBlock + wave;
+        const float a = w13_pair<HC>(x, wsgu, Is, j);
+        if (lane_id() == 0) act_s[j] = a;
+    }
+}
+
+// Routed workgroups [0, K*I/4): wave 0 selects the experts from the logits
+// (the top-k kernel's arithmetic; workgroup 0 also writes ids and weights),
+// then every wave takes (slot u, row pair j).  Shared workgroups: one wave per
+// RPL = 64/LPR rows of the shared down projection (the W2 kernel's
+// arithmetic with weight 1), s[h] in fp32.
+template <int HC, int NPL, int LPR, int CPL>
+__global__ __launch_bounds__(kBlock) void k_expand(
+    const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsd,
+    const float *__restrict__ logits, const float *__restrict__ act_s, int E, int I, int K,
+    int Is, int renormalize, int32_t *__restrict__ ids, float *__restrict__ weights,
+    float *__restrict__ act, float *__restrict__ s_out)
+{
+    constexpr int H = 512 * HC;
+    __shared__ int sh_ids[kMaxTopk];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int routed_blocks = K * (I / kWavesPerBlock);
+    const int b = blockIdx.x;
+    if (b < routed_blocks) {
+        if (wave == 0) {
+            float v[NPL];
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) v[i] = i * kWave + lane < E ? logits[i * kWave + lane] : 0.0f;
+            int my_id;
+            float my_l;
+            const float lmax = wave_topk_vals<NPL>(v, E, K, my_id, my_l);
+            if (lane < K) sh_ids[lane] = my_id;
+            if (b == 0) {
+                const float w = topk_weight_vals<NPL>(v, E, K, renormalize, my_l, lmax);
+                if (lane < K) {
+                    ids[lane] = my_id;
+                    weights[lane] = w;
+                }
+            }
+        }
+        __syncthreads();
+        const int per_expert = I / kWavesPerBlock;
+        const int u = b / per_expert;
+        const int j = (b % per_expert) * kWavesPerBlock + wave;
+        const float a = w13_pair<HC>(x, w13 + (size_t)sh_ids[u] * 2 * I * H, I, j);
+        if (lane == 0) act[(size_t)u * I + j] = a;
+    } else {
+        constexpr int RPL = kWave / LPR;
+        const int r = lane / LPR;
+        const int cl = lane % LPR;
+        const int h = ((b - routed_blocks) * kWavesPerBlock + wave) * RPL + r;
+        const f16x8 *row = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * Is);
+        f16x8 wv[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) wv[c] = stream_load(row + c * LPR + cl);
+        float d = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(act_s + (c * LPR + cl) * 8);
+            d = dot8_f32(wv[c], ap[0], ap[1], d);
+        }
+        const float t = group_sum<LPR>(fmaf(1.0f, d, 0.0f));
+        if (lane == group_holder<LPR>(r)) s_out[h] = t;
+    }
+}
+
+// Routed down projections and the combine, kRWaves waves per workgroup (one
+// workgroup per CU at the full-width shape).  Each wave owns RPL = 64/LPR rows
+// h, LPR lanes per row with CPL 16-byte chunks each (I = 8*LPR*CPL).  The wave
+// first issues its W2 rows for up to 8/CPL experts, then the workgroup stages
+// the activations [K*I] in LDS, then every lane accumulates as the W2 kernel
+// does: acc += w[k] * (its part of row h of W2[e_k] . act_k), experts in
+// routing order; one group reduction; y = fp16(acc + s[h]).
+constexpr int kRWaves = 8;
+constexpr int kRBlock = kRWaves * kWave;
+
+template <int LPR, int CPL>
+__global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ act,
+                                                    const f16 *__restrict__ w2,
+                                                    const int32_t *__restrict__ ids,
+                                                    const float *__restrict__ tw,
+                                                    const float *__restrict__ s_in, int H, int I,
+                                                    int K, f16 *__restrict__ y)
+{
+    extern __shared__ float lds[]; // [K*I] routed activations
+    constexpr int RPL = kWave / LPR;
+    constexpr int BATCH = 8 / CPL;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int r = lane / LPR;
+    const int cl = lane % LPR;
+    const int h = (blockIdx.x * kRWaves + wave) * RPL + r;
+
+    f16x8 wv[BATCH][CPL];
+    const int first = K < BATCH ? K : BATCH;
+#pragma unroll
+    for (int t = 0; t < BATCH; ++t)
+        if (t < first) {
+            const f16x8 *row = reinterpret_cast<const f16x8 *>(w2 + ((size_t)ids[t] * H + h) * I);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
+        }
+    const int n4 = K * I / 4;
+    f32x4 *l4 = reinterpret_cast<f32x4 *>(lds);
+    for (int q = threadIdx.x; q < n4; q += kRBlock) l4[q] = reinterpret_cast<const f32x4 *>(act)[q];
+    __syncthreads();
+
+    float acc = 0.0f;
+    for (int u0 = 0; u0 < K; u0 += BATCH) {
+        const int cnt = K - u0 < BATCH ? K - u0 : BATCH;
+        if (u0 > 0) {
+#pragma unroll
+            for (int t = 0; t < BATCH; ++t)
+                if (t < cnt) {
+                    const f16x8 *row =
+                        reinterpret_cast<const f16x8 *>(w2 + ((size_t)ids[u0 + t] * H + h) * I);
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
+                }
+        }
+#pragma unroll
+        for (int t = 0; t < BATCH; ++t)
+            if (t < cnt) {
+                const int k = u0 + t;
+                const float *ak = lds + (size_t)k * I;
+                float d = 0.0f;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const f32x4 *ap = reinterpret_cast<const f32x4 *>(ak + (c * LPR + cl) * 8);
+                    d = dot8_f32(wv[t][c], ap[0], ap[1], d);
+                }
+                acc = fmaf(tw[k], d, acc);
+            }
+    }
+    const float t = group_sum<LPR>(acc);
+    if (lane == group_holder<LPR>(r)) y[h] = (f16)(s_in ? t + s_in[h] : t);
 }
 
 // ---------------------------------------------------------------- group table only
@@ -1234,6 +1481,110 @@ hipError_t launch_layer(const void *x, const void *wr, const void *w13, const vo
     switch (H / 512) {
     case 2: return launch_layer_h<2>(a, s);
     case 4: return launch_layer_h<4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+// lanes per row of a down-projection GEMV over rows of length n (16-byte chunks)
+static inline int lpr_of(int n) { return n >= 512 ? 64 : n / 8; }
+
+bool lean_ok(int M, int H, int E, int I, int K, int Is)
+{
+    // k_reduce stages [K*I] fp32 in LDS; its workgroups and k_expand's shared
+    // workgroups cover whole row groups of H
+    return M == 1 && E <= kMaxExperts && (size_t)K * I * sizeof(float) <= 64 * 1024 &&
+           H % (kRWaves * (kWave / lpr_of(I))) == 0 &&
+           (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
+}
+
+size_t lean_scratch_bytes(int H) { return (size_t)H * sizeof(float); }
+
+template <int HC, int NPL, int LPR, int CPL>
+static void launch_expand_t(dim3 grid, const void *x, const void *w13, const void *wsd,
+                            const float *logits, const float *act_s, int E, int I, int K, int Is,
+                            int renorm, int32_t *ids, float *w, float *act, float *s_out,
+                            hipStream_t s)
+{
+    hipLaunchKernelGGL((k_expand<HC, NPL, LPR, CPL>), grid, dim3(kBlock), 0, s, (const f16 *)x,
+                       (const f16 *)w13, (const f16 *)wsd, logits, act_s, E, I, K, Is, renorm,
+                       ids, w, act, s_out);
+}
+
+template <int HC, int NPL>
+static void launch_expand_n(dim3 grid, const void *x, const void *w13, const void *wsd,
+                            const float *logits, const float *act_s, int E, int I, int K, int Is,
+                            int renorm, int32_t *ids, float *w, float *act, float *s_out,
+                            hipStream_t s)
+{
+    // the shared down projection's lane mapping (rows of length Is)
+    switch (Is) {
+    case 0:
+    case 512: launch_expand_t<HC, NPL, 64, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 64: launch_expand_t<HC, NPL, 8, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 128: launch_expand_t<HC, NPL, 16, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 256: launch_expand_t<HC, NPL, 32, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 1024: launch_expand_t<HC, NPL, 64, 2>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    default: launch_expand_t<HC, NPL, 64, 4>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    }
+}
+
+template <int HC>
+static hipError_t launch_lean_hc(const void *x, const void *wr, const void *w13, const void *wsgu,
+                                 const void *wsd, int E, int I, int K, int Is, int renorm,
+                                 int32_t *ids, float *w, float *logits, float *act, float *act_s,
+                                 float *s_out, hipStream_t s)
+{
+    const int rb = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((k_router_shared<HC>), dim3(rb + Is / kWavesPerBlock), dim3(kBlock), 0, s,
+                       (const f16 *)x, (const f16 *)wr, (const f16 *)wsgu, E, Is, logits, act_s);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    constexpr int H = 512 * HC;
+    const int shared_blocks = Is ? H / (kWavesPerBlock * (kWave / lpr_of(Is))) : 0;
+    const dim3 grid(K * (I / kWavesPerBlock) + shared_blocks);
+    if (E <= kWave)
+        launch_expand_n<HC, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+    else if (E <= 4 * kWave)
+        launch_expand_n<HC, 4>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+    else
+        launch_expand_n<HC, kMaxExperts / kWave>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+    return last();
+}
+
+template <int LPR, int CPL>
+static hipError_t launch_reduce_t(const float *act, const void *w2, const int32_t *ids,
+                                  const float *w, const float *s_in, int H, int I, int K,
+                                  void *y, hipStream_t s)
+{
+    constexpr int rows = kRWaves * (kWave / LPR);
+    const size_t lds = (size_t)K * I * sizeof(float);
+    hipLaunchKernelGGL((k_reduce<LPR, CPL>), dim3(H / rows), dim3(kRBlock), lds, s, act,
+                       (const f16 *)w2, ids, w, s_in, H, I, K, (f16 *)y);
+    return last();
+}
+
+hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
+                       const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
+                       int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
+                       float *act_s, float *s_out, hipStream_t s)
+{
+    hipError_t err;
+    switch (H / 512) {
+    case 1: err = launch_lean_hc<1>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, s); break;
+    case 2: err = launch_lean_hc<2>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, s); break;
+    case 4: err = launch_lean_hc<4>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, s); break;
+    case 8: err = launch_lean_hc<8>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (err != hipSuccess) return err;
+    const float *s_in = Is ? s_out : nullptr;
+    switch (I) {
+    case 64: return launch_reduce_t<8, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
+    case 128: return launch_reduce_t<16, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
+    case 256: return launch_reduce_t<32, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
+    case 512: return launch_reduce_t<64, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
+    case 1024: return launch_reduce_t<64, 2>(act, w2, ids, w, s_in, H, I, K, y, s);
+    case 2048: return launch_reduce_t<64, 4>(act, w2, ids, w, s_in, H, I, K, y, s);
     }
     return hipErrorInvalidValue;
 }
