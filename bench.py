@@ -9,14 +9,15 @@ SiLU*mul, W2 + weighted combine + shared add).  2.08 GB of weights stream per
 replay, far above the 256 MiB last-level cache, so every replay reads cold
 from HBM.  Inputs are seeded synthetic tensors resident in HBM before timing.
 
-Each layer is one launch of the fused layer kernel (moe_layer_decode); with
---path separate the three entry points run instead (six kernels per layer).
+Each layer is one moe_layer_decode call, three launches at M=1 (router +
+shared gate/up, expand, reduce); with --path separate the three entry points
+run instead (six kernels per layer).
 
 Reported (one JSON line): expert-byte throughput in GB/s (value), us/layer,
 fraction of the 8 TB/s HBM peak, the roofline of the dominant kernel (the
-fused layer kernel, each launch timed with HIP events on the stream it runs
-on) and the fp64 oracle timed on this host's cores on a bounded sample of the
-same layers.
+expand kernel; every kernel of every layer timed with HIP events that the
+library records on the stream the kernels run on) and the fp64 oracle timed on
+this host's cores on a bounded sample of the same layers.
 """
 from __future__ import annotations
 
@@ -33,7 +34,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE decode µs/layer and achieved HBM GB/s (% of MI355X peak), M=1"
 HBM_PEAK_GBS = 8000.0
 LAYERS = 36
-COUNTERS = os.path.join(ROOT, "profiles", "layer_kernel_counters_full_e256_k8_i512.json")
+COUNTERS = os.path.join(ROOT, "profiles", "k_expand_counters_full_e256_k8_i512.json")
+STAGES = ("k_router_shared", "k_expand", "k_reduce")
 KERNEL_SRC = os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", "moe_kernels.hip")
 
 
@@ -50,14 +52,19 @@ def layer_bytes(sh, n_distinct):
     return expert, total
 
 
-def launch_bytes(sh):
-    """Algorithmic bytes of one fused layer launch at M=1 (all K experts distinct):
-    router, K experts' W13 and W2 rows, shared expert, x and y."""
-    return layer_bytes(sh, sh.K)[1]
+def stage_bytes(sh):
+    """Algorithmic bytes of each of the three launches of one layer at M=1 (K
+    distinct experts): weights read once, x once, and the small tensors each
+    kernel reads or writes (logits, activations, s, ids/weights, y)."""
+    H, E, K, I, Is = sh.H, sh.E, sh.K, sh.I, sh.Is
+    router = 2 * E * H + 2 * 2 * Is * H + 2 * H + 4 * E + 4 * Is
+    expand = 2 * K * 2 * I * H + 2 * H * Is + 2 * H + 4 * E + 4 * Is + 4 * K * I + 4 * H + 8 * K
+    reduce = 2 * K * H * I + 4 * K * I + 8 * K + 4 * H + 2 * H
+    return dict(zip(STAGES, (router, expand, reduce)))
 
 
 def counters_traffic():
-    """HBM traffic per launch of the fused layer kernel from the committed rocprofv3
+    """HBM traffic per launch of the expand kernel from the committed rocprofv3
     counter summary, if it was taken on the current kernel source; else None."""
     try:
         c = json.load(open(COUNTERS))
@@ -106,25 +113,42 @@ def cpu_baseline(stack_tensors, sh, budget_s=12.0):
                       "router, top-k, 8 experts, shared expert), %.1f s wall" % (done, el)}
 
 
-def time_launches(layers, reps):
-    """Average duration of one layer launch, with HIP events recorded around each
-    launch on the stream the kernel runs on (cold: the 36 layers rotate)."""
+def time_stages(layers, reps):
+    """Average duration of each of the three kernels of a layer: for each kernel,
+    a hipGraph of that kernel alone for every layer of the stack (inputs left
+    by the full calls before it; the layers rotate, so weights stream cold),
+    replayed `reps` times between two HIP events on the replay stream."""
     import torch
+    import routed_expert_gemv_amd as moe
 
-    stream = torch.cuda.current_stream()
-    evs = []
-    for r in range(reps + 1):
-        for layer in layers:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            layer.forward(stream)
-            b.record(stream)
-            if r > 0:
-                evs.append((a, b))
+    def stage_call(layer, stage):
+        t, sh = layer.t, layer.shape
+        moe.moe_dbg_layer_stage(stage, t["x"], t["wr"], t["w13"], t["w2"], t["wsgu"], t["wsd"],
+                                sh.K, sh.renormalize, layer.topk_ids, layer.topk_w, layer.logits,
+                                layer.y, layer.ws)
+
+    for layer in layers:  # every stage's inputs in place
+        layer.forward()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return sum(ms) / len(ms) * 1e3, len(ms)  # us, launches
+    us = {}
+    for i, name in enumerate(STAGES):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for layer in layers:
+                stage_call(layer, i + 1)
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us[name] = a.elapsed_time(b) * 1e3 / (reps * len(layers))
+        del g
+    return us, reps * len(layers)
 
 
 # ---------------------------------------------------------------- rocprofv3 helpers
@@ -132,10 +156,12 @@ COPY_BYTES = 1 << 30
 
 
 def counters_pass(args):
-    """Workload for `rocprofv3 --pmc`: a plain 1 GiB device copy (calibrates what
-    FETCH_SIZE / WRITE_SIZE read for a known byte count), then the fused layer
-    kernel on every layer of the stack, twice (cold: layers rotate)."""
+    """Workload for `rocprofv3 --pmc`: the library's plain copy kernel over 1 GiB
+    (calibrates what FETCH_SIZE / WRITE_SIZE read for a known byte count), then
+    every layer of the stack through moe_layer_decode, twice (cold: layers
+    rotate)."""
     import torch
+    import routed_expert_gemv_amd as moe
     from routed_expert_gemv_amd import synth
     from routed_expert_gemv_amd.stack import DecodeLayer
 
@@ -143,7 +169,7 @@ def counters_pass(args):
     src = torch.ones(COPY_BYTES // 2, dtype=torch.float16, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        moe.moe_probe_copy(src, dst)
     torch.cuda.synchronize()
     del src, dst
     sh = synth.SHAPES["full_e256_k8_i512"]
@@ -166,21 +192,22 @@ def _read_csv_rows(d, suffix):
 
 
 def summarize_counters(fetch_dir, write_dir, out_path, cmds):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the W13 kernel, scaled by what the
-    same counters read for the 1 GiB copy, into a JSON summary."""
-    def per_kernel(d, counter):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE of the expand kernel (and, for
+    context, the other two), scaled by what the same counters read for the
+    1 GiB copy, into a JSON summary."""
+    def per_kernel(d, counter, kernel="k_expand"):
         rows = _read_csv_rows(d, "counter_collection.csv")
-        w13, copy = [], []
+        mine, copy = [], []
         for r in rows:
             if r.get("Counter_Name") != counter:
                 continue
             v = float(r["Counter_Value"])
             name = r.get("Kernel_Name", "")
-            if "k_layer" in name:
-                w13.append(v)
-            elif "copy" in name.lower():
+            if kernel in name:
+                mine.append(v)
+            elif "k_probe_copy" in name:
                 copy.append(v)
-        return w13, copy
+        return mine, copy
 
     fw, fc = per_kernel(fetch_dir, "FETCH_SIZE")
     ww, wc = per_kernel(write_dir, "WRITE_SIZE")
@@ -193,17 +220,26 @@ def summarize_counters(fetch_dir, write_dir, out_path, cmds):
     write_b = (sum(ww) / len(ww)) * kib / write_scale
     from routed_expert_gemv_amd import synth
     sh = synth.SHAPES["full_e256_k8_i512"]
+    others = {}
+    for k in ("k_router_shared", "k_reduce"):
+        f, _ = per_kernel(fetch_dir, "FETCH_SIZE", k)
+        w, _ = per_kernel(write_dir, "WRITE_SIZE", k)
+        if f and w:
+            others[k] = {"hbm_bytes_per_dispatch": int(round((sum(f) / len(f)) * kib / fetch_scale
+                                                             + (sum(w) / len(w)) * kib / write_scale)),
+                         "algorithmic_bytes_per_dispatch": stage_bytes(sh)[k]}
     res = {
-        "kernel": "k_layer<4,64,1,4> (fused layer kernel, M=1)",
-        "workload": "full-width layer H=2048 E=256 K=8 I=512, M=1, 36 layers rotating",
+        "kernel": "k_expand<4,4,64,1> (routed gate/up + SiLU*mul, shared down), M=1",
+        "workload": "full-width layer H=2048 E=256 K=8 I=512 Is=512, M=1, 36 layers rotating",
         "commands": cmds,
         "fetch_size_kib_per_dispatch": sum(fw) / len(fw),
         "write_size_kib_per_dispatch": sum(ww) / len(ww),
         "copy_fetch_kib": sum(fc) / len(fc), "copy_write_kib": sum(wc) / len(wc),
         "copy_bytes": COPY_BYTES, "fetch_scale": fetch_scale, "write_scale": write_scale,
         "hbm_bytes_per_dispatch": int(round(fetch_b + write_b)),
-        "algorithmic_bytes_per_dispatch": launch_bytes(sh),
+        "algorithmic_bytes_per_dispatch": stage_bytes(sh)["k_expand"],
         "dispatches": len(fw),
+        "other_kernels": others,
         "kernel_source_sha256": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest(),
     }
     with open(out_path, "w") as fh:
@@ -300,15 +336,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=LAYERS)
-    ap.add_argument("--launch-reps", type=int, default=5)
+    ap.add_argument("--launch-reps", type=int, default=10)
     ap.add_argument("--path", choices=("fused", "separate"), default="fused",
-                    help="fused: moe_layer_decode (one launch per layer); separate: the "
+                    help="fused: moe_layer_decode (three launches per layer); separate: the "
                          "three entry points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--counters-pass", action="store_true",
-                    help="run the rocprofv3 --pmc workload (copy calibration + W13 launches)")
+                    help="run the rocprofv3 --pmc workload (copy calibration + layer launches)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
     ap.add_argument("--cmd", action="append", default=[],
@@ -372,11 +408,22 @@ def main():
     gbs_total = total_b / (ms_step * 1e-3) / 1e9
     log("%.3f ms/replay, %.2f us/layer, %.0f GB/s expert bytes" % (ms_step, us_layer, gbs_expert))
 
-    k_us, n_launch = time_launches(layers, args.launch_reps)
-    k_b = launch_bytes(sh)
-    k_gbs = k_b / (k_us * 1e-6) / 1e9
-    traffic = counters_traffic() if args.path == "fused" else None
-    log("layer launch: %.2f us avg over %d launches, %.0f GB/s" % (k_us, n_launch, k_gbs))
+    roof = None
+    if args.path == "fused":
+        st_us, n_launch = time_stages(layers, args.launch_reps)
+        st_b = stage_bytes(sh)
+        dom = max(STAGES, key=lambda k: st_us[k])
+        k_gbs = st_b[dom] / (st_us[dom] * 1e-6) / 1e9
+        log("kernels (HIP events over stage graphs, %d launches each): %s" % (n_launch, ", ".join(
+            "%s %.2f us %.0f GB/s" % (k, st_us[k], st_b[k] / (st_us[k] * 1e-6) / 1e9)
+            for k in STAGES)))
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(k_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                "traffic": counters_traffic() if dom == "k_expand" else None,
+                "avg_launch_us": round(st_us[dom], 3), "bytes_per_launch": st_b[dom],
+                "launches_timed": n_launch,
+                "per_kernel_us": {k: round(v, 3) for k, v in st_us.items()},
+                "per_kernel_bytes": st_b}
 
     out = {
         "metric": METRIC, "value": round(gbs_expert, 1), "unit": "GB/s",
@@ -391,12 +438,7 @@ def main():
         "frac_of_peak": round(gbs_expert / HBM_PEAK_GBS, 4),
         "gbs_total": round(gbs_total, 1),
         "expert_bytes_per_layer": expert_b // args.layers,
-        "roofline": {"kernel": ("k_layer (fused layer kernel: router, top-k, W13 + SiLU, "
-                                "W2 + combine, shared expert), M=1" if args.path == "fused"
-                                else "layer = six kernels (three entry points), M=1"),
-                     "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_us": round(k_us, 3), "bytes_per_launch": k_b},
+        "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_probes:

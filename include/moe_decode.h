@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 #define MOE_MAX_TOKENS 8
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_EXPERTS 1024
@@ -138,32 +138,42 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
  * Results equal the three-call sequence shared_expert, moe_route,
  * moe_decode_fused bit for bit (routing outputs and y), whichever way it runs.
  *
- * For M = 1, H in {1024, 2048}, I <= 1024, Is in {0, I}, K*I <= 8192 and
- * E <= 1024 it is ONE kernel: workgroups take the router, shared-expert
- * gate/up, routed gate/up and down roles by index, and hand logits, the
- * selection and the activations on through device memory; see
- * moe_layer_fused.  Other sizes run the three calls' kernels in sequence.
+ * For M = 1 (K*I <= 16384) it is three launches: the router rows together
+ * with the shared expert's gate/up rows; the routed gate/up rows (each
+ * workgroup selecting the experts from the logits itself) together with the
+ * shared down rows; the routed down rows with the weighted combine.  Other
+ * sizes run the three calls' kernels in sequence.  See moe_layer_launches.
  *   x, w_router, w13, w2  as for moe_route / moe_decode_fused
  *   w_gate_up, w_down     shared expert [2Is, H] / [H, Is], or both NULL (Is ignored)
  *   topk_ids, topk_w, logits  outputs as for moe_route
  *   y          [M, H] fp16 out
- *   ws         >= moe_workspace_bytes(M, H, E, I, K, Is) bytes, ZERO-FILLED before its
- *              first use with this function; the kernel keeps a launch count and
- *              synchronisation counters there between calls.  Calls that share a ws
- *              must not overlap in time.
- * Every wait between workgroups is bounded; a wait that exhausts its poll
- * budget (not expected on an idle GPU) is counted in the workspace, see
- * moe_dbg_layer_diag. */
+ *   ws         >= moe_workspace_bytes(M, H, E, I, K, Is) bytes of device memory;
+ *              scratch only (nothing is kept between calls).  Calls that share a
+ *              ws must not overlap in time. */
 moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13, const void *w2,
                             const void *w_gate_up, const void *w_down, int M, int H, int E, int I,
                             int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
                             float *logits, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* 1 if moe_layer_decode runs as one kernel for these sizes on the current
- * device, 0 if it runs the separate kernels (or the sizes are unsupported). */
-int moe_layer_fused(int M, int H, int E, int I, int K, int Is);
+/* Number of kernels moe_layer_decode enqueues for these sizes (3 on the
+ * M = 1 path), 0 for unsupported sizes or M = 0. */
+int moe_layer_launches(int M, int H, int E, int I, int K, int Is);
 
 /* ---- test-only probes (not part of the decode path) --------------------- */
+
+/* One launch of moe_layer_decode's three-launch path (M = 1) alone, for timing
+ * each kernel: stage 1 = router + shared gate/up (writes logits and the shared
+ * activations to ws), 2 = expand (reads them; writes topk_ids, topk_w, the
+ * routed activations and the shared output), 3 = reduce (reads those; writes
+ * y).  A stage reads what the previous stage left in the same buffers, so
+ * only a full moe_layer_decode call (or stages 1, 2, 3 in order) on them makes
+ * its inputs valid.  Arguments as for moe_layer_decode; MOE_ERR_SHAPE for a
+ * stage outside 1..3 or sizes that do not take the three-launch path. */
+moe_status moe_dbg_layer_stage(int stage, const void *x, const void *w_router, const void *w13,
+                               const void *w2, const void *w_gate_up, const void *w_down, int M,
+                               int H, int E, int I, int K, int Is, int renormalize,
+                               int32_t *topk_ids, float *topk_w, float *logits, void *y, void *ws,
+                               size_t ws_bytes, hipStream_t stream);
 
 /* An empty kernel: launch latency and the gap between hipGraph kernel nodes. */
 moe_status moe_probe_empty(hipStream_t stream);
@@ -174,10 +184,10 @@ moe_status moe_probe_empty(hipStream_t stream);
  * input never produces. */
 moe_status moe_probe_read(const void *src, size_t bytes, float *out, hipStream_t stream);
 
-/* Diagnostics of moe_layer_decode on workspace `ws`, written to out[0..2)
- * (device): out[0] = bounded waits that gave up since the workspace was
- * zero-filled (0 when all went as designed), out[1] = 0 (reserved). */
-moe_status moe_dbg_layer_diag(const void *ws, unsigned *out, hipStream_t stream);
+/* Copies `bytes` (a multiple of 16) from src to dst (device, not overlapping)
+ * with a plain 16-byte load/store kernel: a known read and write byte count,
+ * the calibration for the memory-traffic counters. */
+moe_status moe_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
 /* Sums 64 fp32 values with one wavefront's cross-lane (DPP) reduction, the
  * same routine the GEMV kernels use; out[0] = the sum.  in: [64] device. */

@@ -5,12 +5,12 @@ The compute path is the C-ABI library ``libmoe_decode.so`` built from
 only marshal torch tensors into it.  Importing the package does not load the
 library; the first call does, and raises if it is missing and cannot be built.
 """
-from .api import (MoeError, moe_abi_version, moe_dbg_layer_diag, moe_dbg_w13_silu,
+from .api import (MoeError, moe_abi_version, moe_dbg_layer_stage, moe_dbg_w13_silu,
                   moe_dbg_w2_combine, moe_dbg_wave_sum, moe_decode_fused, moe_layer_decode,
-                  moe_layer_fused, moe_probe_empty, moe_probe_read, moe_route,
+                  moe_layer_launches, moe_probe_copy, moe_probe_empty, moe_probe_read, moe_route,
                   moe_workspace_bytes, shared_expert, workspace)
 
-__all__ = ["MoeError", "moe_abi_version", "moe_dbg_layer_diag", "moe_dbg_w13_silu",
+__all__ = ["MoeError", "moe_abi_version", "moe_dbg_layer_stage", "moe_dbg_w13_silu",
            "moe_dbg_w2_combine", "moe_dbg_wave_sum", "moe_decode_fused", "moe_layer_decode",
-           "moe_layer_fused", "moe_probe_empty", "moe_probe_read", "moe_route",
+           "moe_layer_launches", "moe_probe_copy", "moe_probe_empty", "moe_probe_read", "moe_route",
            "moe_workspace_bytes", "shared_expert", "workspace"]

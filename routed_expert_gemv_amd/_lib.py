@@ -15,8 +15,8 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
                 -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
 EXPORTED = ["moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
             "shared_expert", "moe_decode_fused", "moe_dbg_wave_sum", "moe_dbg_w13_silu",
-            "moe_dbg_w2_combine", "moe_layer_decode", "moe_dbg_layer_diag", "moe_layer_fused",
-            "moe_probe_empty", "moe_probe_read"]
+            "moe_dbg_w2_combine", "moe_layer_decode", "moe_layer_launches", "moe_dbg_layer_stage",
+            "moe_probe_empty", "moe_probe_read", "moe_probe_copy"]
 
 _vp = C.c_void_p
 _i = C.c_int
@@ -55,14 +55,16 @@ def lib() -> C.CDLL:
             L.moe_layer_decode.restype = _i
             L.moe_layer_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp] + [_i] * 7 + \
                 [_vp, _vp, _vp, _vp, _vp, _sz, _vp]
+            L.moe_dbg_layer_stage.restype = _i
+            L.moe_dbg_layer_stage.argtypes = [_i] + L.moe_layer_decode.argtypes
             L.moe_probe_empty.restype = _i
             L.moe_probe_empty.argtypes = [_vp]
+            L.moe_probe_copy.restype = _i
+            L.moe_probe_copy.argtypes = [_vp, _vp, _sz, _vp]
             L.moe_probe_read.restype = _i
             L.moe_probe_read.argtypes = [_vp, _sz, _vp, _vp]
-            L.moe_layer_fused.restype = _i
-            L.moe_layer_fused.argtypes = [_i] * 6
-            L.moe_dbg_layer_diag.restype = _i
-            L.moe_dbg_layer_diag.argtypes = [_vp, _vp, _vp]
+            L.moe_layer_launches.restype = _i
+            L.moe_layer_launches.argtypes = [_i] * 6
             _lib = L
     return _lib
 

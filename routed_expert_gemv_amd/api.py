@@ -7,6 +7,8 @@ library raises MoeError.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import torch
 
 from . import _lib
@@ -204,11 +206,9 @@ def moe_dbg_w2_combine(activated, w2, topk_ids, topk_w, shared_in=None, y=None, 
     return y
 
 
-def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int = 8,
-                     renormalize: bool = True, topk_ids=None, topk_w=None, logits=None, y=None,
-                     ws=None, stream=None):
-    """The whole layer (shared expert, routing, routed experts, combine) in as few
-    launches as the sizes allow.  Returns (y, topk_ids, topk_w, logits)."""
+def _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids, topk_w,
+                logits, y, ws):
+    """Checks and marshals moe_layer_decode's arguments; returns (outputs, C args)."""
     _dev_tensor("x", x, torch.float16, 2)
     _dev_tensor("w_router", w_router, torch.float16, 2)
     _dev_tensor("w13", w13, torch.float16, 3)
@@ -241,33 +241,57 @@ def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int =
     if ws is None:
         ws = workspace(max(M, 1), H, E, I, K, Is, dev)
     _dev_tensor("ws", ws, torch.uint8)
-    st = _lib.lib().moe_layer_decode(_ptr(x), _ptr(w_router), _ptr(w13), _ptr(w2), _ptr(w_gate_up),
-                                     _ptr(w_down), M, H, E, I, K, Is, int(bool(renormalize)),
-                                     _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y), _ptr(ws),
-                                     ws.numel(), _stream(stream, dev))
+    args = (_ptr(x), _ptr(w_router), _ptr(w13), _ptr(w2), _ptr(w_gate_up), _ptr(w_down), M, H, E,
+            I, K, Is, int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
+            _ptr(ws), ws.numel())
+    return (y, topk_ids, topk_w, logits), args
+
+
+def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int = 8,
+                     renormalize: bool = True, topk_ids=None, topk_w=None, logits=None, y=None,
+                     ws=None, stream=None):
+    """The whole layer (shared expert, routing, routed experts, combine) in as few
+    launches as the sizes allow.  Returns (y, topk_ids, topk_w, logits)."""
+    out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
+                            topk_w, logits, y, ws)
+    st = _lib.lib().moe_layer_decode(*args, _stream(stream, x.device))
     _check("moe_layer_decode", st)
-    return y, topk_ids, topk_w, logits
+    return out
 
 
-def moe_layer_fused(M: int, H: int, E: int, I: int, K: int, Is: int = 0) -> bool:
-    """Whether moe_layer_decode runs as one kernel for these sizes on the current device."""
-    return bool(_lib.lib().moe_layer_fused(M, H, E, I, K, Is))
+def moe_dbg_layer_stage(stage: int, x, w_router, w13, w2, w_gate_up=None, w_down=None,
+                        K: int = 8, renormalize: bool = True, topk_ids=None, topk_w=None,
+                        logits=None, y=None, ws=None, stream=None):
+    """Benchmark probe: launch `stage` (1 router + shared gate/up, 2 expand,
+    3 reduce) of moe_layer_decode's three-launch path alone, on buffers a full
+    call already filled.  Returns (y, topk_ids, topk_w, logits)."""
+    out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
+                            topk_w, logits, y, ws)
+    st = _lib.lib().moe_dbg_layer_stage(int(stage), *args, _stream(stream, x.device))
+    _check("moe_dbg_layer_stage", st)
+    return out
 
 
-def moe_dbg_layer_diag(ws, stream=None) -> dict:
-    """Test probe: diagnostics moe_layer_decode keeps in the workspace."""
-    _dev_tensor("ws", ws, torch.uint8)
-    out = torch.zeros(2, dtype=torch.int32, device=ws.device)
-    st = _lib.lib().moe_dbg_layer_diag(_ptr(ws), _ptr(out), _stream(stream, ws.device))
-    _check("moe_dbg_layer_diag", st)
-    v = out.tolist()
-    return {"timeouts": v[0]}
+def moe_layer_launches(M: int, H: int, E: int, I: int, K: int, Is: int = 0) -> int:
+    """Number of kernels moe_layer_decode enqueues for these sizes (0 if unsupported)."""
+    return int(_lib.lib().moe_layer_launches(M, H, E, I, K, Is))
 
 
 def moe_probe_empty(stream=None):
     """Bench probe: launch one empty kernel."""
     dev = torch.device("cuda", torch.cuda.current_device())
     _check("moe_probe_empty", _lib.lib().moe_probe_empty(_stream(stream, dev)))
+
+
+def moe_probe_copy(src, dst, stream=None) -> None:
+    """Test probe: plain device copy of src into dst (same byte size)."""
+    _dev_tensor("src", src, torch.float16)
+    _dev_tensor("dst", dst, torch.float16)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError("src and dst differ in size")
+    _check("moe_probe_copy", _lib.lib().moe_probe_copy(_ptr(src), _ptr(dst), n,
+                                                        _stream(stream, src.device)))
 
 
 def moe_probe_read(buf, out=None, stream=None):

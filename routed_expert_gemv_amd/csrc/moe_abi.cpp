@@ -22,17 +22,49 @@ size_t routed_ws_bytes(int M, int I, int K)
     return kRoutedActOffset + align256((size_t)M * K * I * sizeof(float));
 }
 
-// moe_layer_decode also needs the fused kernel's partial outputs, after the rest
-size_t layer_ws_bytes(int M, int H, int E, int I, int K, int Is)
-{
-    size_t n = routed_ws_bytes(M, I, K);
-    if (layer_fusable(M, H, E, I, K, Is)) n += align256(layer_partial_bytes(H, E, I, K, Is));
-    return n;
-}
-
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 } // namespace
+
+// moe_layer_decode; stage > 0 (three-launch path only) runs that launch alone.
+static moe_status layer_decode(const void *x, const void *w_router, const void *w13,
+                               const void *w2, const void *w_gate_up, const void *w_down, int M,
+                               int H, int E, int I, int K, int Is, int renormalize,
+                               int32_t *topk_ids, float *topk_w, float *logits, void *y, void *ws,
+                               size_t ws_bytes, int stage, hipStream_t stream)
+{
+    const bool shared = w_gate_up != nullptr || w_down != nullptr;
+    if (!shared) Is = 0;
+    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (shared && !i_ok(Is)))
+        return MOE_ERR_SHAPE;
+    if (M == 0) return MOE_OK;
+    if (!x || !w_router || !w13 || !w2 || !topk_ids || !topk_w || !logits || !y || !ws ||
+        (shared && (!w_gate_up || !w_down)))
+        return MOE_ERR_NULL;
+    if (!al(x, 16) || !al(w_router, 16) || !al(w13, 16) || !al(w2, 16) || !al(topk_ids, 4) ||
+        !al(topk_w, 4) || !al(logits, 4) || !al(y, 2) || !al(ws, 256) ||
+        (shared && (!al(w_gate_up, 16) || !al(w_down, 16))))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < routed_ws_bytes(M, I, K)) return MOE_ERR_WORKSPACE;
+    if (stage != 0 && (stage < 1 || stage > 3 || !lean_ok(M, H, E, I, K, Is))) return MOE_ERR_SHAPE;
+    char *base = static_cast<char *>(ws);
+    float *act_s = reinterpret_cast<float *>(base);
+    float *act = reinterpret_cast<float *>(base + kRoutedActOffset);
+    if (lean_ok(M, H, E, I, K, Is))
+        return hip_status(launch_lean(x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is,
+                                      renormalize, topk_ids, topk_w, logits, y, act, act_s,
+                                      reinterpret_cast<float *>(base + kSharedOutOffset), stage,
+                                      stream));
+    float *s_out = shared ? reinterpret_cast<float *>(base + kSharedOutOffset) : nullptr;
+    hipError_t err = hipSuccess;
+    if (shared) err = launch_shared(x, w_gate_up, w_down, M, H, Is, s_out, act_s, stream);
+    if (err == hipSuccess)
+        err = launch_route(x, w_router, M, H, E, K, renormalize, topk_ids, topk_w, logits, stream);
+    if (err == hipSuccess)
+        err = launch_fused(x, w13, w2, topk_ids, topk_w, s_out, M, H, E, I, K, y, act,
+                           reinterpret_cast<GroupTable *>(base + kGroupOffset), stream);
+    return hip_status(err);
+}
 
 extern "C" {
 
@@ -54,7 +86,7 @@ const char *moe_status_str(moe_status s)
 size_t moe_workspace_bytes(int M, int H, int E, int I, int K, int Is)
 {
     if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (Is != 0 && !i_ok(Is))) return 0;
-    return layer_ws_bytes(M < 1 ? 1 : M, H, E, I, K, Is);
+    return routed_ws_bytes(M < 1 ? 1 : M, I, K);
 }
 
 moe_status moe_route(const void *x, const void *w_router, int M, int H, int E, int K,
@@ -106,52 +138,28 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
                             int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
                             float *logits, void *y, void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    const bool shared = w_gate_up != nullptr || w_down != nullptr;
-    if (!shared) Is = 0;
-    if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (shared && !i_ok(Is)))
-        return MOE_ERR_SHAPE;
-    if (M == 0) return MOE_OK;
-    if (!x || !w_router || !w13 || !w2 || !topk_ids || !topk_w || !logits || !y || !ws ||
-        (shared && (!w_gate_up || !w_down)))
-        return MOE_ERR_NULL;
-    if (!al(x, 16) || !al(w_router, 16) || !al(w13, 16) || !al(w2, 16) || !al(topk_ids, 4) ||
-        !al(topk_w, 4) || !al(logits, 4) || !al(y, 2) || !al(ws, 256) ||
-        (shared && (!al(w_gate_up, 16) || !al(w_down, 16))))
-        return MOE_ERR_ALIGN;
-    if (ws_bytes < layer_ws_bytes(M, H, E, I, K, Is)) return MOE_ERR_WORKSPACE;
-    char *base = static_cast<char *>(ws);
-    float *act_s = reinterpret_cast<float *>(base);
-    float *act = reinterpret_cast<float *>(base + kRoutedActOffset);
-    if (lean_ok(M, H, E, I, K, Is))
-        return hip_status(launch_lean(x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is,
-                                      renormalize, topk_ids, topk_w, logits, y, act, act_s,
-                                      reinterpret_cast<float *>(base + kSharedOutOffset), stream));
-    if (layer_fusable(M, H, E, I, K, Is))
-        return hip_status(launch_layer(
-            x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is, renormalize, topk_ids, topk_w,
-            logits, y, base, reinterpret_cast<float *>(base + routed_ws_bytes(M, I, K)), stream));
-    float *s_out = shared ? reinterpret_cast<float *>(base + kSharedOutOffset) : nullptr;
-    hipError_t err = hipSuccess;
-    if (shared) err = launch_shared(x, w_gate_up, w_down, M, H, Is, s_out, act_s, stream);
-    if (err == hipSuccess)
-        err = launch_route(x, w_router, M, H, E, K, renormalize, topk_ids, topk_w, logits, stream);
-    if (err == hipSuccess)
-        err = launch_fused(x, w13, w2, topk_ids, topk_w, s_out, M, H, E, I, K, y, act,
-                           reinterpret_cast<GroupTable *>(base + kGroupOffset), stream);
-    return hip_status(err);
+    return layer_decode(x, w_router, w13, w2, w_gate_up, w_down, M, H, E, I, K, Is, renormalize,
+                        topk_ids, topk_w, logits, y, ws, ws_bytes, 0, stream);
 }
 
-int moe_layer_fused(int M, int H, int E, int I, int K, int Is)
+moe_status moe_dbg_layer_stage(int stage, const void *x, const void *w_router, const void *w13,
+                               const void *w2, const void *w_gate_up, const void *w_down, int M,
+                               int H, int E, int I, int K, int Is, int renormalize,
+                               int32_t *topk_ids, float *topk_w, float *logits, void *y, void *ws,
+                               size_t ws_bytes, hipStream_t stream)
+{
+    if (stage < 1 || stage > 3) return MOE_ERR_SHAPE;
+    return layer_decode(x, w_router, w13, w2, w_gate_up, w_down, M, H, E, I, K, Is, renormalize,
+                        topk_ids, topk_w, logits, y, ws, ws_bytes, stage, stream);
+}
+
+int moe_layer_launches(int M, int H, int E, int I, int K, int Is)
 {
     if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (Is != 0 && !i_ok(Is))) return 0;
-    return layer_fusable(M, H, E, I, K, Is) ? 1 : 0;
-}
-
-moe_status moe_dbg_layer_diag(const void *ws, unsigned *out, hipStream_t stream)
-{
-    if (!ws || !out) return MOE_ERR_NULL;
-    if (!al(ws, 256) || !al(out, 4)) return MOE_ERR_ALIGN;
-    return hip_status(launch_read_layer_diag(static_cast<const char *>(ws), out, stream));
+    if (M == 0) return 0;
+    if (lean_ok(M, H, E, I, K, Is)) return 3;
+    // shared_expert (2) + moe_route (2) + moe_decode_fused (2)
+    return (Is ? 2 : 0) + 2 + 2;
 }
 
 moe_status moe_probe_empty(hipStream_t stream) { return hip_status(launch_probe_empty(stream)); }
@@ -161,6 +169,13 @@ moe_status moe_probe_read(const void *src, size_t bytes, float *out, hipStream_t
     if (!src || !out) return MOE_ERR_NULL;
     if (!al(src, 16) || !al(out, 4) || bytes % 16) return MOE_ERR_ALIGN;
     return hip_status(launch_probe_read(src, bytes, out, stream));
+}
+
+moe_status moe_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t stream)
+{
+    if (!src || !dst) return MOE_ERR_NULL;
+    if (!al(src, 16) || !al(dst, 16) || bytes % 16) return MOE_ERR_ALIGN;
+    return hip_status(launch_probe_copy(src, dst, bytes, stream));
 }
 
 moe_status moe_dbg_wave_sum(const float *in, float *out, hipStream_t stream)

@@ -25,32 +25,15 @@ struct GroupTable {
     signed char u_slot[kMaxSlots][kMaxTokens];
 };
 
-// Fused layer kernel: synchronisation words (one per 256-byte line) and limits.
-constexpr int kFusedMaxAct = 8192 + 2048; // K*I + Is activations staged in LDS (fp32)
-struct alignas(256) SyncWord {
-    unsigned v;
-};
-struct LayerSync {
-    SyncWord epoch;        // launches completed on this workspace
-    SyncWord blocks_done;  // workgroups finished in the current launch
-    SyncWord timeouts;     // bounded waits that gave up (diagnostic)
-    SyncWord router_done;  // router workgroups whose logits are stored
-    SyncWord shared_hint;  // shared gate/up workgroups that issued their stores
-    SyncWord w13_hint[16]; // routed W13 workgroups that issued their stores
-};
-
 // Workspace layout (bytes from the start of ws, 256-byte aligned regions):
 //   [0, kSharedActBytes)                  shared-expert activations [M, Is] fp32
 //   [kGroupOffset, +sizeof(GroupTable))   GroupTable
-//   [kSyncOffset, +sizeof(LayerSync))     LayerSync (zero before first use)
 //   [kSharedOutOffset, +M*H*4)            shared-expert output [M, H] fp32
 //   [kRoutedActOffset, +M*K*I*4)          routed activations [M, K, I] fp32
-//   [kRoutedActOffset + M*K*I*4, ...)     tagged logits / activations of the fused kernel
 constexpr size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 constexpr size_t kSharedActBytes = (size_t)kMaxTokens * kMaxInter * sizeof(float);
 constexpr size_t kGroupOffset = align256(kSharedActBytes);
-constexpr size_t kSyncOffset = kGroupOffset + align256(sizeof(GroupTable));
-constexpr size_t kSharedOutOffset = kSyncOffset + align256(sizeof(LayerSync));
+constexpr size_t kSharedOutOffset = kGroupOffset + align256(sizeof(GroupTable));
 constexpr size_t kSharedOutBytes = (size_t)kMaxTokens * 4096 * sizeof(float);
 constexpr size_t kRoutedActOffset = kSharedOutOffset + align256(kSharedOutBytes);
 
@@ -68,21 +51,17 @@ hipError_t launch_fused(const void *x, const void *w13, const void *w2, const in
 hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids, const float *tw,
                             const float *shared_in, int M, int H, int E, int I, int K, void *y,
                             GroupTable *table, hipStream_t s);
-bool layer_fusable(int M, int H, int E, int I, int K, int Is);
-size_t layer_partial_bytes(int H, int E, int I, int K, int Is);
-hipError_t launch_layer(const void *x, const void *wr, const void *w13, const void *w2,
-                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
-                        int renorm, int32_t *ids, float *w, float *logits, void *y, char *ws,
-                        float *partial, hipStream_t s);
-hipError_t launch_read_layer_diag(const char *ws, unsigned *out, hipStream_t s);
+hipError_t launch_probe_empty(hipStream_t s);
+hipError_t launch_probe_read(const void *src, size_t bytes, float *out, hipStream_t s);
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
+hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s);
+// The layer at M = 1 in three launches (router + shared gate/up, expand, reduce);
+// stage 0 runs all three, stage 1..3 that launch alone.
 bool lean_ok(int M, int H, int E, int I, int K, int Is);
 hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
                        int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
-                       float *act_s, float *s_out, hipStream_t s);
-hipError_t launch_probe_empty(hipStream_t s);
-hipError_t launch_probe_read(const void *src, size_t bytes, float *out, hipStream_t s);
-hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s);
+                       float *act_s, float *s_out, int stage, hipStream_t s);
 
 } // namespace moe
 

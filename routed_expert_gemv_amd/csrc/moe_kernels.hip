@@ -273,18 +273,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Loads of data another workgroup of the same launch published: agent-scope
-// coherent (they bypass stale cache lines without a cache-wide invalidate).
-__device__ __forceinline__ float ld_agent(const float *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void st_agent(float *p, float v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ int wave_min_i32(int v)
 {
     v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
@@ -574,416 +562,6 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
 }
 
 
-// ---------------------------------------------------------------- fused layer (M = 1)
-// The whole layer in one launch.  Workgroups of 16 waves take roles by index:
-//   [0, nR)          router: one wave per two expert rows -> logits; the last
-//                    router workgroup (by arrival) selects the experts once
-//                    and publishes ids + weights, tagged, in kRouteCopies
-//                    copies (so the pollers spread over many lines)
-//   [.., +nS)        shared expert gate/up + SiLU*mul: one wave per row pair
-//                    -> tagged act_s
-//   [.., +nW13)      routed W13 + SiLU*mul: waits for the routing, one wave
-//                    per (expert, row pair) -> tagged act
-//   [.., +nW2)       routed W2 + combine + shared down: loads its shared-down
-//                    rows, waits for the routing, loads its W2 rows (up to 8
-//                    experts in flight), gathers the tagged activations into
-//                    LDS and writes y.
-// A hand-off between workgroups has to go through memory (on this GPU only
-// agent-coherent loads see another workgroup's stores) and anything waiting
-// for a store acknowledgement queues behind the weight stream.  So published
-// values are 64-bit agent-coherent stores of (epoch << 32 | value bits) and a
-// consumer checks every value's tag (the epoch is read at launch start; the
-// last workgroup to finish advances it).  Counters are only hints, bumped
-// without waiting for the stores, that tell a consumer when gathering is
-// likely to succeed at once; the tags decide.  The one exception is the
-// routing: router workgroups drain their logit stores before taking a ticket,
-// so the last ticket holder reads every logit.
-// A workgroup only waits on lower-numbered ones (dispatch is in index order
-// per XCD, so the lowest unfinished one can always run), and every wait is
-// bounded (kSpinLimit polls, counted in sync->timeouts when exhausted).
-// Arithmetic per element is the same device code as the separate kernels
-// (same lane mapping, same reduction trees, same order), so the results equal
-// shared_expert + moe_route + moe_decode_fused bit for bit.
-constexpr unsigned kSpinLimit = 1u << 17; // ~0.1 s of polling at most
-constexpr int kLWaves = 16;
-constexpr int kLBlock = kLWaves * kWave;
-constexpr int kRouterRowsPerWave = 2;
-constexpr int kRouteCopies = 32;
-constexpr int kRouteWords = 2 * kMaxTopk; // ids then weights, tagged
-constexpr int kHints = 16;
-
-typedef unsigned long long u64;
-
-struct LayerArgs {
-    const f16 *x, *wr, *w13, *w2, *wsgu, *wsd;
-    int E, I, K, Is, renormalize;
-    int nR, nS, nW13, nW2;
-    float *logits;
-    int32_t *ids;
-    float *weights;
-    f16 *y;
-    LayerSync *sync;
-    float *logits_c;  // [E] logits for the selecting workgroup (agent-coherent)
-    u64 *t_route;     // [kRouteCopies][kRouteWords]
-    u64 *t_act;       // [K * I]
-    u64 *t_act_s;     // [Is]
-};
-
-__device__ __forceinline__ unsigned ld_relaxed(const unsigned *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ u64 ld_tag(const u64 *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void st_tag(u64 *p, unsigned ep, uint32_t bits)
-{
-    __hip_atomic_store(p, ((u64)ep << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void bump(unsigned *p)
-{
-    __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void nap(unsigned it)
-{
-    if (it < 2) __builtin_amdgcn_s_sleep(2);
-    else __builtin_amdgcn_s_sleep(8);
-}
-
-__device__ __forceinline__ int lwave() { return (int)(threadIdx.x / kWave); }
-
-__device__ __forceinline__ void count_timeout(LayerSync *sync) { bump(&sync->timeouts.v); }
-
-template <int HC, int NPL>
-__device__ __forceinline__ void role_router(const LayerArgs &a, int b, unsigned ep, int *sh_last)
-{
-    constexpr int H = 512 * HC;
-    const int e0 = (b * kLWaves + lwave()) * kRouterRowsPerWave;
-    if (e0 < a.E) {
-        f16x8 xv[HC], w0[HC], w1[HC];
-        load_x<HC>(a.x, xv);
-        load_row<HC>(a.wr + (size_t)e0 * H, w0);
-        const bool two = e0 + 1 < a.E;
-        if (two) load_row<HC>(a.wr + (size_t)(e0 + 1) * H, w1);
-        const float t0 = row_dot<HC>(w0, xv);
-        const float t1 = two ? row_dot<HC>(w1, xv) : 0.0f;
-        if (lane_id() == 0) {
-            st_agent(a.logits_c + e0, t0);
-            a.logits[e0] = t0;
-            if (two) {
-                st_agent(a.logits_c + e0 + 1, t1);
-                a.logits[e0 + 1] = t1;
-            }
-        }
-    }
-    // drain the logit stores, then take a ticket; the last ticket selects
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0)
-        *sh_last = __hip_atomic_fetch_add(&a.sync->router_done.v, 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == (unsigned)a.nR - 1u;
-    __syncthreads();
-    if (!*sh_last || lwave() != 0) return;
-    const int lane = lane_id();
-    float v[NPL];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        const int e = i * kWave + lane;
-        v[i] = e < a.E ? ld_agent(a.logits_c + e) : 0.0f;
-    }
-    int my_id;
-    float my_l;
-    const float lmax = wave_topk_vals<NPL>(v, a.E, a.K, my_id, my_l);
-    const float my_w = topk_weight_vals<NPL>(v, a.E, a.K, a.renormalize, my_l, lmax);
-    if (lane < a.K) {
-        a.ids[lane] = my_id;
-        a.weights[lane] = my_w;
-    }
-    // kRouteCopies copies of [ids | weights], lanes 0..K-1 and 16..16+K-1 of each
-    for (int c = 0; c < kRouteCopies; c += 2) {
-        const int copy = c + lane / 32, slot = lane % 32;
-        const int k = slot % kMaxTopk;
-        const int idk = __shfl(my_id, k);
-        const float wk = __shfl(my_w, k);
-        if (k < a.K)
-            st_tag(a.t_route + (size_t)copy * kRouteWords + slot, ep,
-                   slot < kMaxTopk ? (uint32_t)idk : __builtin_bit_cast(uint32_t, wk));
-    }
-}
-
-template <int HC>
-__device__ __forceinline__ void role_shared_gate_up(const LayerArgs &a, int b, unsigned ep)
-{
-    constexpr int H = 512 * HC;
-    const int j = b * kLWaves + lwave();
-    f16x8 xv[HC], wg[HC], wu[HC];
-    load_x<HC>(a.x, xv);
-    load_row<HC>(a.wsgu + (size_t)j * H, wg);
-    load_row<HC>(a.wsgu + (size_t)(a.Is + j) * H, wu);
-    const float g = row_dot<HC>(wg, xv);
-    const float up = row_dot<HC>(wu, xv);
-    if (lane_id() == 0) st_tag(a.t_act_s + j, ep, __builtin_bit_cast(uint32_t, silu_mul(g, up)));
-    __syncthreads();
-    if (threadIdx.x == 0) bump(&a.sync->shared_hint.v);
-}
-
-// Wave 0 polls this workgroup's copy of the published routing until every
-// entry carries `ep`; lane k of every wave then holds expert k's id and weight.
-__device__ __forceinline__ void block_route(const LayerArgs &a, int b, unsigned ep, int *sh_ids,
-                                            float *sh_w, int &my_id, float &my_w)
-{
-    if (lwave() == 0) {
-        const int lane = lane_id();
-        const int k = lane % kMaxTopk;
-        const bool mine = lane < kRouteWords && k < a.K;
-        const u64 *src = a.t_route + (size_t)(b % kRouteCopies) * kRouteWords + lane;
-        u64 t = 0;
-        unsigned it = 0;
-        for (; it < kSpinLimit; ++it) {
-            bool ok = true;
-            if (mine) {
-                t = ld_tag(src);
-                ok = (unsigned)(t >> 32) == ep;
-            }
-            if (__ballot(!ok) == 0ull) break;
-            nap(it);
-        }
-        if (it == kSpinLimit && lane == 0) count_timeout(a.sync);
-        if (mine) {
-            if (lane < kMaxTopk) sh_ids[k] = (int)(uint32_t)t;
-            else sh_w[k] = __builtin_bit_cast(float, (uint32_t)t);
-        }
-    }
-    __syncthreads();
-    const int k = lane_id() < a.K ? lane_id() : 0;
-    my_id = sh_ids[k];
-    my_w = sh_w[k];
-}
-
-template <int HC>
-__device__ __forceinline__ void role_w13(const LayerArgs &a, int b, unsigned ep, int *sh_ids,
-                                         float *sh_w)
-{
-    constexpr int H = 512 * HC;
-    const int per_expert = a.I / kLWaves;
-    const int u = b / per_expert;
-    const int j = (b % per_expert) * kLWaves + lwave();
-    f16x8 xv[HC];
-    load_x<HC>(a.x, xv);
-    int my_id;
-    float my_w;
-    block_route(a, b, ep, sh_ids, sh_w, my_id, my_w);
-    const int expert = __builtin_amdgcn_readlane(my_id, u);
-    const f16 *base = a.w13 + (size_t)expert * 2 * a.I * H;
-    f16x8 wg[HC], wu[HC];
-    load_row<HC>(base + (size_t)j * H, wg);
-    load_row<HC>(base + (size_t)(a.I + j) * H, wu);
-    const float g = row_dot<HC>(wg, xv);
-    const float up = row_dot<HC>(wu, xv);
-    if (lane_id() == 0)
-        st_tag(a.t_act + (size_t)u * a.I + j, ep, __builtin_bit_cast(uint32_t, silu_mul(g, up)));
-    __syncthreads();
-    if (threadIdx.x == 0) bump(&a.sync->w13_hint[b % kHints].v);
-}
-
-// thread 0 polls the hint counters until the producers have (probably) published
-__device__ __forceinline__ void block_hint_wait(const LayerArgs &a)
-{
-    if (threadIdx.x == 0) {
-        unsigned it = 0;
-        for (; it < kSpinLimit; ++it) {
-            unsigned n = 0;
-            for (int i = 0; i < kHints; ++i) n += ld_relaxed(&a.sync->w13_hint[i].v);
-            if (n >= (unsigned)a.nW13 && ld_relaxed(&a.sync->shared_hint.v) >= (unsigned)a.nS) break;
-            nap(it);
-        }
-        if (it == kSpinLimit) count_timeout(a.sync);
-    }
-    __syncthreads();
-}
-
-// Buffer resource over `bytes` bytes at `p` (raw addressing; loads past the end
-// return 0 instead of touching memory).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *p, int bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
-}
-
-// Cache policy of the relaxed agent-scope loads above (sc1), as a buffer-load
-// argument: the same agent-coherent read.
-constexpr int kAuxAgent = 16;
-
-// all threads gather the n tagged values src[0..n) into lds[0..n) until every
-// one carries `ep` (each thread re-reads only its own missing entries).  Entry
-// i = threadIdx.x + q * kLBlock: one per-thread offset, the q part is scalar,
-// so the poll holds no per-entry addresses in vector registers.
-__device__ __forceinline__ void block_gather(const u64 *src, int n, float *lds, unsigned ep,
-                                             LayerSync *sync)
-{
-    constexpr int kPer = 8; // entries per thread tracked in a bit mask (n <= 8 * kLBlock)
-    const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(src, n * (int)sizeof(u64));
-    const int voff = (int)threadIdx.x * (int)sizeof(u64);
-    unsigned missing = 0;
-    for (int q = 0; q < kPer; ++q)
-        if ((int)threadIdx.x + q * kLBlock < n) missing |= 1u << q;
-    unsigned it = 0;
-    for (; it < kSpinLimit; ++it) {
-#pragma unroll
-        for (int q = 0; q < kPer; ++q)
-            if (missing & (1u << q)) {
-                const auto t = __builtin_amdgcn_raw_buffer_load_b64(
-                    rsrc, voff, q * kLBlock * (int)sizeof(u64), kAuxAgent);
-                if (t[1] == ep) {
-                    lds[threadIdx.x + q * kLBlock] = __builtin_bit_cast(float, t[0]);
-                    missing &= ~(1u << q);
-                }
-            }
-        if (__syncthreads_count(missing != 0) == 0) break;
-        nap(it);
-    }
-    if (it == kSpinLimit && threadIdx.x == 0) count_timeout(sync);
-    __syncthreads();
-}
-
-template <int LPR, int CPL>
-__device__ __forceinline__ void role_w2(const LayerArgs &a, int b, unsigned ep, float *lds,
-                                        int *sh_ids, float *sh_w)
-{
-    constexpr int RPL = kWave / LPR;
-    constexpr int BATCH = 8 / CPL; // W2 chunks in flight per lane: 8 (registers)
-    const int H = a.nW2 * kLWaves * RPL;
-    const int lane = lane_id();
-    const int wave = lwave();
-    const int r = lane / LPR;
-    const int cl = lane % LPR;
-    const int h = (b * kLWaves + wave) * RPL + r;
-    const bool shared = a.nS > 0;
-
-    // shared down rows do not depend on routing: load them first
-    f16x8 ws[CPL];
-    if (shared) {
-        const f16x8 *row = reinterpret_cast<const f16x8 *>(a.wsd + (size_t)h * a.Is);
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) ws[c] = stream_load(row + c * LPR + cl);
-    }
-    int my_id;
-    float my_w;
-    block_route(a, b, ep, sh_ids, sh_w, my_id, my_w);
-    // first batch of routed W2 rows in flight before the activations are gathered
-    f16x8 wv[BATCH][CPL];
-    const int first = a.K < BATCH ? a.K : BATCH;
-#pragma unroll
-    for (int t = 0; t < BATCH; ++t)
-        if (t < first) {
-            const int e = __builtin_amdgcn_readlane(my_id, t);
-            const f16x8 *row = reinterpret_cast<const f16x8 *>(a.w2 + ((size_t)e * H + h) * a.I);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
-        }
-    block_hint_wait(a);
-    const int n_act = a.K * a.I;
-    block_gather(a.t_act, n_act, lds, ep, a.sync);
-    if (shared) block_gather(a.t_act_s, a.Is, lds + n_act, ep, a.sync);
-
-    float acc = 0.0f;
-    for (int u0 = 0; u0 < a.K; u0 += BATCH) {
-        const int cnt = a.K - u0 < BATCH ? a.K - u0 : BATCH;
-        if (u0 > 0) {
-#pragma unroll
-            for (int t = 0; t < BATCH; ++t)
-                if (t < cnt) {
-                    const int e = __builtin_amdgcn_readlane(my_id, u0 + t);
-                    const f16x8 *row =
-                        reinterpret_cast<const f16x8 *>(a.w2 + ((size_t)e * H + h) * a.I);
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
-                }
-        }
-#pragma unroll
-        for (int t = 0; t < BATCH; ++t)
-            if (t < cnt) {
-                const int k = u0 + t;
-                const float wt = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), k));
-                const float *ak = lds + (size_t)k * a.I;
-                float d = 0.0f;
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const f32x4 *ap = reinterpret_cast<const f32x4 *>(ak + (c * LPR + cl) * 8);
-                    d = dot8_f32(wv[t][c], ap[0], ap[1], d);
-                }
-                acc = fmaf(wt, d, acc);
-            }
-    }
-    float acc_s = 0.0f;
-    if (shared) {
-        const float *as = lds + n_act;
-        float d = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const f32x4 *ap = reinterpret_cast<const f32x4 *>(as + (c * LPR + cl) * 8);
-            d = dot8_f32(ws[c], ap[0], ap[1], d);
-        }
-        acc_s = fmaf(1.0f, d, 0.0f);
-    }
-    const float t = group_sum<LPR>(acc);
-    const float ts = group_sum<LPR>(acc_s);
-    if (lane == group_holder<LPR>(r)) a.y[h] = (f16)(shared ? t + ts : t);
-}
-
-template <int HC, int LPR, int CPL, int NPL>
-__global__ __launch_bounds__(kLBlock, 8) void k_layer(LayerArgs a)
-{
-    extern __shared__ float lds[];
-    __shared__ int sh_ids[kMaxTopk];
-    __shared__ float sh_w[kMaxTopk];
-    __shared__ unsigned sh_ep;
-    __shared__ int sh_last;
-    const int b = blockIdx.x;
-    if (threadIdx.x == 0) sh_ep = ld_relaxed(&a.sync->epoch.v) + 1u;
-    __syncthreads();
-    const unsigned ep = sh_ep;
-    if (b < a.nR)
-        role_router<HC, NPL>(a, b, ep, &sh_last);
-    else if (b < a.nR + a.nS)
-        role_shared_gate_up<HC>(a, b - a.nR, ep);
-    else if (b < a.nR + a.nS + a.nW13)
-        role_w13<HC>(a, b - a.nR - a.nS, ep, sh_ids, sh_w);
-    else
-        role_w2<LPR, CPL>(a, b - a.nR - a.nS - a.nW13, ep, lds, sh_ids, sh_w);
-
-    // the last workgroup of the launch re-arms the counters and advances the epoch
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned total = (unsigned)(a.nR + a.nS + a.nW13 + a.nW2);
-        const unsigned old = __hip_atomic_fetch_add(&a.sync->blocks_done.v, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (old == total - 1) {
-            __hip_atomic_store(&a.sync->router_done.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.sync->shared_hint.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            for (int i = 0; i < kHints; ++i)
-                __hip_atomic_store(&a.sync->w13_hint[i].v, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.sync->blocks_done.v, 0u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.sync->epoch.v, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-}
-
-__global__ void k_read_layer_diag(const LayerSync *__restrict__ sync, unsigned *__restrict__ out)
-{
-    if (threadIdx.x == 0) {
-        out[0] = ld_relaxed(&sync->timeouts.v);
-        out[1] = 0u;
-    }
-}
-
 // ---------------------------------------------------------------- layer path (M = 1)
 // Three launches for a whole layer at M = 1, plain grids of independent
 // workgroups (the kernel boundaries are the only hand-offs):
@@ -1212,6 +790,26 @@ __global__ __launch_bounds__(256) void k_probe_read(const f16x8 *__restrict__ sr
     if (acc == 1.25e-3f) out[0] = acc; // keeps the loads; never true for zero-filled input
 }
 
+// Plain device copy of n16 16-byte chunks (8 per thread): reads and writes a
+// known byte count, the calibration for the memory-traffic counters.
+__global__ __launch_bounds__(256) void k_probe_copy(const f16x8 *__restrict__ src,
+                                                    f16x8 *__restrict__ dst, size_t n16)
+{
+    constexpr int L = 8;
+    const size_t base = (size_t)blockIdx.x * blockDim.x * L + threadIdx.x;
+    f16x8 v[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const size_t idx = base + (size_t)i * blockDim.x;
+        if (idx < n16) v[i] = stream_load(src + idx);
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const size_t idx = base + (size_t)i * blockDim.x;
+        if (idx < n16) dst[idx] = v[i];
+    }
+}
+
 __global__ __launch_bounds__(kWave) void k_dbg_wave_sum(const float *__restrict__ in,
                                                          float *__restrict__ out)
 {
@@ -1392,6 +990,17 @@ hipError_t launch_probe_read(const void *src, size_t bytes, float *out, hipStrea
     return last();
 }
 
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t s)
+{
+    const size_t n16 = bytes / 16;
+    const size_t per_block = 256 * 8;
+    const unsigned blocks = (unsigned)((n16 + per_block - 1) / per_block);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_probe_copy, dim3(blocks), dim3(256), 0, s, (const f16x8 *)src,
+                       (f16x8 *)dst, n16);
+    return last();
+}
+
 hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s)
 {
     hipLaunchKernelGGL(k_dbg_wave_sum, dim3(1), dim3(kWave), 0, s, in, out);
@@ -1399,92 +1008,7 @@ hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s)
 }
 
 
-// ---------------------------------------------------------------- fused layer launcher
-bool layer_fusable(int M, int H, int E, int I, int K, int Is)
-{
-    // block_gather tracks at most 8 entries per thread: K*I and Is <= 8 * kLBlock
-    return M == 1 && (H == 1024 || H == 2048) && I <= 1024 && (Is == 0 || Is == I) &&
-           K * I <= 8 * kLBlock && K * I + Is <= kFusedMaxAct && E <= kMaxExperts;
-}
-
-template <int HC, int LPR, int CPL>
-static hipError_t launch_layer_t(const LayerArgs &a, hipStream_t s)
-{
-    const int blocks = a.nR + a.nS + a.nW13 + a.nW2;
-    const size_t lds = (size_t)(a.K * a.I + a.Is) * sizeof(float);
-    if (a.E <= kWave)
-        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, 1>), dim3(blocks), dim3(kLBlock), lds, s, a);
-    else if (a.E <= 4 * kWave)
-        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, 4>), dim3(blocks), dim3(kLBlock), lds, s, a);
-    else
-        hipLaunchKernelGGL((k_layer<HC, LPR, CPL, kMaxExperts / kWave>), dim3(blocks),
-                           dim3(kLBlock), lds, s, a);
-    return last();
-}
-
-template <int HC>
-static hipError_t launch_layer_h(const LayerArgs &a, hipStream_t s)
-{
-    switch (a.I) {
-    case 64: return launch_layer_t<HC, 8, 1>(a, s);
-    case 128: return launch_layer_t<HC, 16, 1>(a, s);
-    case 256: return launch_layer_t<HC, 32, 1>(a, s);
-    case 512: return launch_layer_t<HC, 64, 1>(a, s);
-    case 1024: return launch_layer_t<HC, 64, 2>(a, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-size_t layer_partial_bytes(int, int E, int I, int K, int Is)
-{
-    // logits, tagged routing copies, tagged routed and shared activations
-    return align256((size_t)E * sizeof(float)) +
-           align256((size_t)kRouteCopies * kRouteWords * sizeof(u64)) +
-           align256((size_t)K * I * sizeof(u64)) + align256((size_t)Is * sizeof(u64));
-}
-
-hipError_t launch_layer(const void *x, const void *wr, const void *w13, const void *w2,
-                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
-                        int renorm, int32_t *ids, float *w, float *logits, void *y, char *ws,
-                        float *partial, hipStream_t s)
-{
-    LayerArgs a;
-    a.x = (const f16 *)x;
-    a.wr = (const f16 *)wr;
-    a.w13 = (const f16 *)w13;
-    a.w2 = (const f16 *)w2;
-    a.wsgu = (const f16 *)wsgu;
-    a.wsd = (const f16 *)wsd;
-    a.E = E;
-    a.I = I;
-    a.K = K;
-    a.Is = wsgu ? Is : 0;
-    a.renormalize = renorm;
-    a.nR = (E + kLWaves * kRouterRowsPerWave - 1) / (kLWaves * kRouterRowsPerWave);
-    a.nS = a.Is / kLWaves;
-    a.nW13 = K * (I / kLWaves);
-    const int lpr = I >= 512 ? kWave : I / 8;
-    a.nW2 = H / ((kWave / lpr) * kLWaves);
-    a.logits = logits;
-    a.ids = ids;
-    a.weights = w;
-    a.y = (f16 *)y;
-    a.sync = reinterpret_cast<LayerSync *>(ws + kSyncOffset);
-    char *t = reinterpret_cast<char *>(partial);
-    a.logits_c = reinterpret_cast<float *>(t);
-    t += align256((size_t)E * sizeof(float));
-    a.t_route = reinterpret_cast<u64 *>(t);
-    t += align256((size_t)kRouteCopies * kRouteWords * sizeof(u64));
-    a.t_act = reinterpret_cast<u64 *>(t);
-    t += align256((size_t)K * I * sizeof(u64));
-    a.t_act_s = reinterpret_cast<u64 *>(t);
-    switch (H / 512) {
-    case 2: return launch_layer_h<2>(a, s);
-    case 4: return launch_layer_h<4>(a, s);
-    }
-    return hipErrorInvalidValue;
-}
-
+// ---------------------------------------------------------------- layer path launchers
 // lanes per row of a down-projection GEMV over rows of length n (16-byte chunks)
 static inline int lpr_of(int n) { return n >= 512 ? 64 : n / 8; }
 
@@ -1496,8 +1020,6 @@ bool lean_ok(int M, int H, int E, int I, int K, int Is)
            H % (kRWaves * (kWave / lpr_of(I))) == 0 &&
            (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
 }
-
-size_t lean_scratch_bytes(int H) { return (size_t)H * sizeof(float); }
 
 template <int HC, int NPL, int LPR, int CPL>
 static void launch_expand_t(dim3 grid, const void *x, const void *w13, const void *wsd,
@@ -1532,13 +1054,17 @@ template <int HC>
 static hipError_t launch_lean_hc(const void *x, const void *wr, const void *w13, const void *wsgu,
                                  const void *wsd, int E, int I, int K, int Is, int renorm,
                                  int32_t *ids, float *w, float *logits, float *act, float *act_s,
-                                 float *s_out, hipStream_t s)
+                                 float *s_out, int stage, hipStream_t s)
 {
     const int rb = (E + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((k_router_shared<HC>), dim3(rb + Is / kWavesPerBlock), dim3(kBlock), 0, s,
-                       (const f16 *)x, (const f16 *)wr, (const f16 *)wsgu, E, Is, logits, act_s);
-    hipError_t err = last();
-    if (err != hipSuccess) return err;
+    if (stage == 0 || stage == 1) {
+        hipLaunchKernelGGL((k_router_shared<HC>), dim3(rb + Is / kWavesPerBlock), dim3(kBlock), 0,
+                           s, (const f16 *)x, (const f16 *)wr, (const f16 *)wsgu, E, Is, logits,
+                           act_s);
+        const hipError_t err = last();
+        if (err != hipSuccess || stage == 1) return err;
+    }
+    if (stage != 0 && stage != 2) return hipSuccess;
     constexpr int H = 512 * HC;
     const int shared_blocks = Is ? H / (kWavesPerBlock * (kWave / lpr_of(Is))) : 0;
     const dim3 grid(K * (I / kWavesPerBlock) + shared_blocks);
@@ -1566,17 +1092,21 @@ static hipError_t launch_reduce_t(const float *act, const void *w2, const int32_
 hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
                        int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
-                       float *act_s, float *s_out, hipStream_t s)
+                       float *act_s, float *s_out, int stage, hipStream_t s)
 {
-    hipError_t err;
-    switch (H / 512) {
-    case 1: err = launch_lean_hc<1>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, s); break;
-    case 2: err = launch_lean_hc<2>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, s); break;
-    case 4: err = launch_lean_hc<4>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, s); break;
-    case 8: err = launch_lean_hc<8>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, s); break;
-    default: return hipErrorInvalidValue;
+    // stage 0: the three launches; 1, 2, 3: that launch alone
+    if (stage < 0 || stage > 3) return hipErrorInvalidValue;
+    hipError_t err = hipSuccess;
+    if (stage <= 2) {
+        switch (H / 512) {
+        case 1: err = launch_lean_hc<1>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, stage, s); break;
+        case 2: err = launch_lean_hc<2>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, stage, s); break;
+        case 4: err = launch_lean_hc<4>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, stage, s); break;
+        case 8: err = launch_lean_hc<8>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, stage, s); break;
+        default: return hipErrorInvalidValue;
+        }
+        if (err != hipSuccess || stage != 0) return err;
     }
-    if (err != hipSuccess) return err;
     const float *s_in = Is ? s_out : nullptr;
     switch (I) {
     case 64: return launch_reduce_t<8, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
@@ -1587,13 +1117,6 @@ hipError_t launch_lean(const void *x, const void *wr, const void *w13, const voi
     case 2048: return launch_reduce_t<64, 4>(act, w2, ids, w, s_in, H, I, K, y, s);
     }
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_read_layer_diag(const char *ws, unsigned *out, hipStream_t s)
-{
-    hipLaunchKernelGGL(k_read_layer_diag, dim3(1), dim3(kWave), 0, s,
-                       reinterpret_cast<const LayerSync *>(ws + kSyncOffset), out);
-    return last();
 }
 
 } // namespace moe

@@ -1,9 +1,9 @@
 """One decode layer's buffers and call sequence, and a hipGraph of many layers.
 
-A layer runs either as moe_layer_decode (one fused launch where the sizes
-allow) or as the three entry points on one stream: shared_expert (independent
-of routing, so it goes first), moe_route, moe_decode_fused (which adds the
-shared output before its single fp16 rounding).  A stack captures every
+A layer runs either as moe_layer_decode (three launches at M = 1) or as the
+three entry points on one stream: shared_expert (independent of routing, so it
+goes first), moe_route, moe_decode_fused (which adds the shared output before
+its single fp16 rounding).  A stack captures every
 layer's launches into one hipGraph (torch.cuda.CUDAGraph drives stream
 capture; the captured nodes are this library's kernels), so one replay is one
 host call.
@@ -19,8 +19,8 @@ from .synth import LayerShape
 class DecodeLayer:
     """Weights, inputs and preallocated outputs of one layer (all on one device).
 
-    forward() runs the layer through moe_layer_decode (one launch where the sizes
-    allow); forward_separate() issues the three entry points one after another.
+    forward() runs the layer through moe_layer_decode (three launches at M = 1);
+    forward_separate() issues the three entry points one after another.
     """
 
     def __init__(self, tensors: dict, shape: LayerShape, fused: bool = True):

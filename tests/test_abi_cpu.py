@@ -27,7 +27,7 @@ def declared_functions():
 def test_library_builds_and_loads():
     assert os.path.exists(build.LIB) or build.build(force=True)
     L = _lib.lib()
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_every_declared_symbol_is_exported():
@@ -120,6 +120,9 @@ def test_fused_validation():
 
 def test_debug_probe_validation():
     L = _lib.lib()
+    assert L.moe_probe_copy(None, FAKE, 16, None) == -1
+    assert L.moe_probe_copy(FAKE, FAKE + 8, 16, None) == -3
+    assert L.moe_probe_copy(FAKE, FAKE, 24, None) == -3
     assert L.moe_dbg_wave_sum(None, FAKE, None) == -1
     assert L.moe_dbg_wave_sum(FAKE + 1, FAKE, None) == -3
     assert L.moe_dbg_w13_silu(FAKE, FAKE, FAKE, 1, 2048, 256, 512, 8, None, FAKE, 1 << 20,
@@ -165,3 +168,27 @@ def test_margin_guard_redraws_until_separated():
     # the accepted margin exceeds twice the worst-case fp32 logit error of every token
     assert np.all(margin > 2 * bound)
     assert np.all(margin > cases.required_margin(t, sh))
+
+
+def test_layer_launch_counts():
+    L = _lib.lib()
+    assert L.moe_layer_launches(1, 2048, 256, 512, 8, 512) == 3    # M = 1: three launches
+    assert L.moe_layer_launches(1, 2048, 256, 512, 8, 0) == 3
+    assert L.moe_layer_launches(2, 2048, 256, 512, 8, 512) == 6    # separate kernels
+    assert L.moe_layer_launches(1, 2048, 16, 2048, 16, 0) == 4     # K*I above the LDS stage
+    assert L.moe_layer_launches(0, 2048, 256, 512, 8, 512) == 0
+    assert L.moe_layer_launches(9, 2048, 256, 512, 8, 512) == 0
+
+
+def test_layer_stage_probe_validation():
+    L = _lib.lib()
+
+    def call(stage, M=1, H=2048):
+        return L.moe_dbg_layer_stage(stage, FAKE, FAKE, FAKE, FAKE, None, None, M, H, 256, 512, 8,
+                                     0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+
+    assert call(0) == -2 and call(4) == -2
+    assert call(2, M=2) == -2          # not the three-launch path
+    assert call(2, H=2000) == -2
+    assert L.moe_dbg_layer_stage(2, None, FAKE, FAKE, FAKE, None, None, 1, 2048, 256, 512, 8, 0, 1,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
