@@ -695,8 +695,10 @@ __global__ __launch_bounds__(kBlock) void k_expand(
 // routing order; one group reduction; y = fp16(acc + s[h]).
 constexpr int kRWaves = 8;
 constexpr int kRBlock = kRWaves * kWave;
+constexpr int kMaxStaged = 16384; // K*I fp32 values staged in LDS (64 KB)
 
-template <int LPR, int CPL>
+// STAGE: 16-byte activation loads per thread, ceil(K*I / (4 * kRBlock)).
+template <int LPR, int CPL, int STAGE>
 __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ act,
                                                     const f16 *__restrict__ w2,
                                                     const int32_t *__restrict__ ids,
@@ -713,33 +715,47 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
     const int cl = lane % LPR;
     const int h = (blockIdx.x * kRWaves + wave) * RPL + r;
 
+    // Everything this wave reads from memory is requested up front: ids and
+    // weights (lane k holds slot k), s[h], then its W2 rows of a whole batch.
+    // Batch slots past K reload the last expert's row (a cache hit, unused),
+    // so the loads need no branches and all stay ahead of the staging below.
+    const int my_id = lane < K ? ids[lane] : 0;
+    const float my_tw = lane < K ? tw[lane] : 0.0f;
+    const float s_h = s_in ? s_in[h] : 0.0f;
     f16x8 wv[BATCH][CPL];
-    const int first = K < BATCH ? K : BATCH;
+    auto load_batch = [&](int u0) {
 #pragma unroll
-    for (int t = 0; t < BATCH; ++t)
-        if (t < first) {
-            const f16x8 *row = reinterpret_cast<const f16x8 *>(w2 + ((size_t)ids[t] * H + h) * I);
+        for (int t = 0; t < BATCH; ++t) {
+            const int k = u0 + t < K ? u0 + t : K - 1;
+            const int e = __builtin_amdgcn_readlane(my_id, k);
+            const f16x8 *row = reinterpret_cast<const f16x8 *>(w2 + ((size_t)e * H + h) * I);
 #pragma unroll
             for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
         }
+    };
+    load_batch(0);
+    // stage act: a thread's loads all in flight before it writes LDS (indices
+    // past the end re-read the last chunk instead of branching)
     const int n4 = K * I / 4;
     f32x4 *l4 = reinterpret_cast<f32x4 *>(lds);
-    for (int q = threadIdx.x; q < n4; q += kRBlock) l4[q] = reinterpret_cast<const f32x4 *>(act)[q];
+    const f32x4 *a4 = reinterpret_cast<const f32x4 *>(act);
+    f32x4 st[STAGE];
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i) {
+        const int q = threadIdx.x + i * kRBlock;
+        st[i] = a4[q < n4 ? q : n4 - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < STAGE; ++i) {
+        const int q = threadIdx.x + i * kRBlock;
+        if (q < n4) l4[q] = st[i];
+    }
     __syncthreads();
 
     float acc = 0.0f;
     for (int u0 = 0; u0 < K; u0 += BATCH) {
+        if (u0 > 0) load_batch(u0);
         const int cnt = K - u0 < BATCH ? K - u0 : BATCH;
-        if (u0 > 0) {
-#pragma unroll
-            for (int t = 0; t < BATCH; ++t)
-                if (t < cnt) {
-                    const f16x8 *row =
-                        reinterpret_cast<const f16x8 *>(w2 + ((size_t)ids[u0 + t] * H + h) * I);
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
-                }
-        }
 #pragma unroll
         for (int t = 0; t < BATCH; ++t)
             if (t < cnt) {
@@ -751,11 +767,13 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
                     const f32x4 *ap = reinterpret_cast<const f32x4 *>(ak + (c * LPR + cl) * 8);
                     d = dot8_f32(wv[t][c], ap[0], ap[1], d);
                 }
-                acc = fmaf(tw[k], d, acc);
+                const float wk = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_tw), k));
+                acc = fmaf(wk, d, acc);
             }
     }
     const float t = group_sum<LPR>(acc);
-    if (lane == group_holder<LPR>(r)) y[h] = (f16)(s_in ? t + s_in[h] : t);
+    if (lane == group_holder<LPR>(r)) y[h] = (f16)(s_in ? t + s_h : t);
 }
 
 // ---------------------------------------------------------------- group table only
@@ -1016,7 +1034,7 @@ bool lean_ok(int M, int H, int E, int I, int K, int Is)
 {
     // k_reduce stages [K*I] fp32 in LDS; its workgroups and k_expand's shared
     // workgroups cover whole row groups of H
-    return M == 1 && E <= kMaxExperts && (size_t)K * I * sizeof(float) <= 64 * 1024 &&
+    return M == 1 && E <= kMaxExperts && K * I <= kMaxStaged &&
            H % (kRWaves * (kWave / lpr_of(I))) == 0 &&
            (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
 }
@@ -1084,8 +1102,18 @@ static hipError_t launch_reduce_t(const float *act, const void *w2, const int32_
 {
     constexpr int rows = kRWaves * (kWave / LPR);
     const size_t lds = (size_t)K * I * sizeof(float);
-    hipLaunchKernelGGL((k_reduce<LPR, CPL>), dim3(H / rows), dim3(kRBlock), lds, s, act,
-                       (const f16 *)w2, ids, w, s_in, H, I, K, (f16 *)y);
+    const int stage = (K * I / 4 + kRBlock - 1) / kRBlock;
+    const dim3 grid(H / rows), block(kRBlock);
+    const f16 *w2h = (const f16 *)w2;
+    f16 *yh = (f16 *)y;
+    if (stage <= 1)
+        hipLaunchKernelGGL((k_reduce<LPR, CPL, 1>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
+    else if (stage <= 2)
+        hipLaunchKernelGGL((k_reduce<LPR, CPL, 2>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
+    else if (stage <= 4)
+        hipLaunchKernelGGL((k_reduce<LPR, CPL, 4>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
+    else
+        hipLaunchKernelGGL((k_reduce<LPR, CPL, 8>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
     return last();
 }
 
