@@ -284,31 +284,25 @@ __device__ __forceinline__ int wave_min_i32(int v)
     return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Top-K of E <= 64*NPL logits held by the wave: v[i] is the logit of expert
-// i*64 + lane (ignored where that is >= E).  Lane k < K receives the k-th
-// selected expert id and its logit; returns the largest logit (wave-uniform).
-// Each lane first sorts its NPL (key, id) pairs by descending key, stably, so
-// equal keys keep ascending ids; then every round takes the largest head key
-// over the wave, the lowest id among the heads holding it (a second reduction
-// only when several lanes tie), and that lane pops its head.
-template <int NPL>
-__device__ __forceinline__ float wave_topk_vals(const float (&v)[NPL], int E, int K, int &my_id,
-                                                float &my_l)
+// Top-K over the wave of N (key, id) pairs per lane (key 0 = no entry; ids
+// distinct): lane k < K receives the k-th largest key and its id, equal keys
+// ordered by ascending id.  Each lane first sorts its pairs by descending key,
+// ascending id (odd-even transposition, swapping only strictly out-of-order
+// neighbours: stable for pairs that arrive in ascending id order, and ties
+// between pairs in any order are decided by the id test); then every round
+// takes the largest head key over the wave, the lowest id among the heads
+// holding it (a second reduction only when several lanes tie), and that lane
+// pops its head.
+template <int N>
+__device__ __forceinline__ void wave_topk_keys(uint32_t (&key)[N], int (&id)[N], int K,
+                                               uint32_t &my_key, int &my_id)
 {
     const int lane = lane_id();
-    uint32_t key[NPL];
-    int id[NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        id[i] = i * kWave + lane;
-        key[i] = id[i] < E ? order_key(v[i]) : 0u;
-    }
-    // odd-even transposition sort, swapping only strictly smaller keys upward (stable)
+    for (int r = 0; r < N; ++r)
 #pragma unroll
-    for (int r = 0; r < NPL; ++r)
-#pragma unroll
-        for (int i = r & 1; i + 1 < NPL; i += 2)
-            if (key[i] < key[i + 1]) {
+        for (int i = r & 1; i + 1 < N; i += 2)
+            if (key[i] < key[i + 1] || (key[i] == key[i + 1] && id[i] > id[i + 1])) {
                 const uint32_t tk = key[i];
                 key[i] = key[i + 1];
                 key[i + 1] = tk;
@@ -316,9 +310,8 @@ __device__ __forceinline__ float wave_topk_vals(const float (&v)[NPL], int E, in
                 id[i] = id[i + 1];
                 id[i + 1] = ti;
             }
-    float lmax = 0.0f;
+    my_key = 0u;
     my_id = 0;
-    my_l = 0.0f;
     for (int k = 0; k < K; ++k) {
         const uint32_t m = wave_max_u32(key[0]);
         const uint64_t b = __ballot(key[0] == m);
@@ -330,20 +323,37 @@ __device__ __forceinline__ float wave_topk_vals(const float (&v)[NPL], int E, in
         }
         if (lane == winner) {
 #pragma unroll
-            for (int i = 0; i + 1 < NPL; ++i) {
+            for (int i = 0; i + 1 < N; ++i) {
                 key[i] = key[i + 1];
                 id[i] = id[i + 1];
             }
-            key[NPL - 1] = 0u;
+            key[N - 1] = 0u;
         }
-        const float lv = key_value(m);
-        if (k == 0) lmax = lv;
         if (lane == k) {
+            my_key = m;
             my_id = wid;
-            my_l = lv;
         }
     }
-    return lmax;
+}
+
+// Top-K of E <= 64*NPL logits held by the wave: v[i] is the logit of expert
+// i*64 + lane (ignored where that is >= E).  Lane k < K receives the k-th
+// selected expert id and its logit; returns the largest logit (wave-uniform).
+template <int NPL>
+__device__ __forceinline__ float wave_topk_vals(const float (&v)[NPL], int E, int K, int &my_id,
+                                                float &my_l)
+{
+    uint32_t key[NPL];
+    int id[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        id[i] = i * kWave + lane_id();
+        key[i] = id[i] < E ? order_key(v[i]) : 0u;
+    }
+    uint32_t my_key;
+    wave_topk_keys<NPL>(key, id, K, my_key, my_id);
+    my_l = my_key ? key_value(my_key) : 0.0f;
+    return key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
 }
 
 // Routing weight of the slot held by this lane (valid in lanes < K): softmax
@@ -628,8 +638,8 @@ __global__ __launch_bounds__(kBlock) void k_router_shared(const f16 *__restrict_
 // Routed workgroups [0, K*I/4): wave 0 selects the experts from the logits
 // (the top-k kernel's arithmetic; workgroup 0 also writes ids and weights),
 // then every wave takes (slot u, row pair j).  Shared workgroups: one wave per
-// RPL = 64/LPR rows of the shared down projection (the W2 kernel's
-// arithmetic with weight 1), s[h] in fp32.
+// RPL = 64/LPR rows of the shared down projection (the W2 kernel's arithmetic
+// with weight 1), s[h] in fp32.
 template <int HC, int NPL, int LPR, int CPL>
 __global__ __launch_bounds__(kBlock) void k_expand(
     const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsd,
@@ -752,25 +762,37 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
     }
     __syncthreads();
 
+    // Per slot: d = this lane's part of row h of W2[e_k] . act_k; then
+    // acc += w_k * d in routing order.  A full batch computes its BATCH
+    // independent d first (no branches, so their chains interleave).
+    auto slot_dot = [&](int t, int k) {
+        const float *ak = lds + (size_t)k * I;
+        float d = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(ak + (c * LPR + cl) * 8);
+            d = dot8_f32(wv[t][c], ap[0], ap[1], d);
+        }
+        return d;
+    };
+    auto weight = [&](int k) {
+        return __builtin_bit_cast(float,
+                                  __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_tw), k));
+    };
     float acc = 0.0f;
     for (int u0 = 0; u0 < K; u0 += BATCH) {
         if (u0 > 0) load_batch(u0);
-        const int cnt = K - u0 < BATCH ? K - u0 : BATCH;
+        if (K - u0 >= BATCH) {
+            float d[BATCH];
 #pragma unroll
-        for (int t = 0; t < BATCH; ++t)
-            if (t < cnt) {
-                const int k = u0 + t;
-                const float *ak = lds + (size_t)k * I;
-                float d = 0.0f;
+            for (int t = 0; t < BATCH; ++t) d[t] = slot_dot(t, u0 + t);
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const f32x4 *ap = reinterpret_cast<const f32x4 *>(ak + (c * LPR + cl) * 8);
-                    d = dot8_f32(wv[t][c], ap[0], ap[1], d);
-                }
-                const float wk = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_tw), k));
-                acc = fmaf(wk, d, acc);
-            }
+            for (int t = 0; t < BATCH; ++t) acc = fmaf(weight(u0 + t), d[t], acc);
+        } else {
+#pragma unroll
+            for (int t = 0; t < BATCH; ++t)
+                if (t < K - u0) acc = fmaf(weight(u0 + t), slot_dot(t, u0 + t), acc);
+        }
     }
     const float t = group_sum<LPR>(acc);
     if (lane == group_holder<LPR>(r)) y[h] = (f16)(s_in ? t + s_h : t);
