@@ -172,7 +172,8 @@ def counters_pass(args):
         moe.moe_probe_copy(src, dst)
     torch.cuda.synchronize()
     del src, dst
-    sh = synth.SHAPES["full_e256_k8_i512"]
+    sh = synth.SHAPES["full_e256_k8_i512" if args.tokens == 1 else
+                      "batch%d_e256_k8_i512" % args.tokens]
     layers = [DecodeLayer(synth.draw_layer(sh, s, dev), sh) for s in range(args.layers)]
     for _ in range(2):
         for l in layers:
@@ -336,6 +337,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--tokens", type=int, default=1, choices=(1, 2, 4, 8),
+                    help="tokens per layer: 1 (the default workload) or a small decode batch "
+                         "(each token routed on its own; distinct experts read once)")
     ap.add_argument("--launch-reps", type=int, default=10)
     ap.add_argument("--path", choices=("fused", "separate"), default="fused",
                     help="fused: moe_layer_decode (three launches per layer); separate: the "
@@ -375,7 +379,8 @@ def main():
     if args.counters_pass:
         counters_pass(args)
         return
-    sh = synth.SHAPES["full_e256_k8_i512"]
+    sh = synth.SHAPES["full_e256_k8_i512" if args.tokens == 1 else
+                      "batch%d_e256_k8_i512" % args.tokens]
 
     log("drawing %d layers (seeds 0..%d) on %s" % (args.layers, args.layers - 1, dev))
     t0 = time.perf_counter()
@@ -409,7 +414,7 @@ def main():
     log("%.3f ms/replay, %.2f us/layer, %.0f GB/s expert bytes" % (ms_step, us_layer, gbs_expert))
 
     roof = None
-    if args.path == "fused":
+    if args.path == "fused" and sh.M == 1:
         st_us, n_launch = time_stages(layers, args.launch_reps)
         st_b = stage_bytes(sh)
         dom = max(STAGES, key=lambda k: st_us[k])
@@ -430,8 +435,11 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "36-layer full-width MoE decode stack as one hipGraph: M=1, "
-                               "H=2048, E=256, top-8 renormalised, I=512, shared Is=512, fp16",
+        "config": {"workload": "%d-layer full-width MoE decode stack as one hipGraph: M=%d, "
+                               "H=2048, E=256, top-8 renormalised, I=512, shared Is=512, fp16"
+                               % (args.layers, sh.M),
+                   "tokens": sh.M,
+                   "distinct_experts_per_layer": round(sum(n_distinct) / len(n_distinct), 2),
                    "layers": args.layers, "layer_seeds": "0..%d" % (args.layers - 1),
                    "path": args.path},
         "us_per_layer": round(us_layer, 3),
@@ -446,7 +454,7 @@ def main():
         out["probes"] = probes(dev)
         log("probes: %s" % out["probes"])
         out["frac_of_read_probe"] = round(gbs_expert / out["probes"]["read_2GiB_GBs"], 4)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and sh.M == 1:
         log("timing the fp64 oracle on the host (~%.0f s)" % args.cpu_budget)
         out["cpu_baseline"] = cpu_baseline(tensors, sh, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -156,23 +156,7 @@ __device__ __forceinline__ GroupScan<MT> group_scan(const int32_t *ids, int M, i
     return g;
 }
 
-// The entry of U at index u, read from the lane that holds it (wave-uniform).
-template <int MT>
-__device__ __forceinline__ void group_pick(const GroupScan<MT> &g, int u, int &expert,
-                                           unsigned &mask, int (&slot)[MT])
-{
-    const uint64_t h0 = __ballot(g.first[0] && g.rank[0] == u);
-    const uint64_t h1 = __ballot(g.first[1] && g.rank[1] == u);
-    const int q = h0 ? 0 : 1;
-    const int src = h0 ? __builtin_ctzll(h0) : __builtin_ctzll(h1);
-    expert = __builtin_amdgcn_readlane(q == 0 ? g.v[0] : g.v[1], src);
-    mask = (unsigned)__builtin_amdgcn_readlane(q == 0 ? (int)g.mask[0] : (int)g.mask[1], src);
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        slot[m] = __builtin_amdgcn_readlane(q == 0 ? g.slot[0][m] : g.slot[1][m], src);
-}
-
-// Store U (ids, token masks, slots) for the W2 kernel.
+// Store U (ids, token masks, slots) for the W13 and W2 kernels.
 template <int MT>
 __device__ __forceinline__ void group_store(const GroupScan<MT> &g, GroupTable *table)
 {
@@ -406,12 +390,11 @@ __global__ __launch_bounds__(kWave) void k_topk(const float *__restrict__ logits
 // and activated = silu(gate) * up is stored (fp32) at act[m, slot, j].
 //
 // SHARED: the shared expert (one "expert" at `w13`, every token, slot 0).
-template <int HC, int MT, bool SHARED>
+template <int HC, bool SHARED>
 __global__ __launch_bounds__(kBlock) void k_w13_silu(const f16 *__restrict__ x,
                                                      const f16 *__restrict__ w13,
-                                                     const int32_t *__restrict__ ids, int M,
-                                                     int I, int K, float *__restrict__ act,
-                                                     GroupTable *__restrict__ table)
+                                                     const int32_t *__restrict__ ids, int I,
+                                                     float *__restrict__ act)
 {
     constexpr int H = 512 * HC;
     const int lane = lane_id();
@@ -419,6 +402,48 @@ __global__ __launch_bounds__(kBlock) void k_w13_silu(const f16 *__restrict__ x,
     const int blocks_per_expert = I / kWavesPerBlock;
     const int u = blockIdx.x / blocks_per_expert;
     const int j = (blockIdx.x % blocks_per_expert) * kWavesPerBlock + wave;
+    const int expert = SHARED ? 0 : ids[u];
+
+    // x first (L2-resident, shared by every wave), then the two weight rows
+    const f16 *base = w13 + (size_t)expert * 2 * I * H;
+    const f16x8 *grow = reinterpret_cast<const f16x8 *>(base + (size_t)j * H);
+    const f16x8 *urow = reinterpret_cast<const f16x8 *>(base + (size_t)(I + j) * H);
+    f16x8 xv[HC], wg[HC], wu[HC];
+    load_x<HC>(x, xv);
+#pragma unroll
+    for (int c = 0; c < HC; ++c) {
+        wg[c] = stream_load(grow + c * kWave + lane);
+        wu[c] = stream_load(urow + c * kWave + lane);
+    }
+    const float g = row_dot<HC>(wg, xv);
+    const float up = row_dot<HC>(wu, xv);
+    if (lane == 0) act[(size_t)(SHARED ? 0 : u) * I + j] = silu_mul(g, up);
+}
+
+// The same for M > 1 tokens.  The distinct selected experts U (with each
+// one's token mask and slots) come from the group table; a workgroup takes
+// expert u and kRowsPerBlockM row pairs of it, kRowsPerWaveM per wave (rows
+// j0 + i*4, the next pair's loads issued before the current pair's
+// arithmetic).  x [M, H] is staged in LDS once per workgroup; for every token
+// that routes to the expert: act[m, slot, j] = silu(gate . x_m) * (up . x_m),
+// the single-token arithmetic.
+// SHARED: the shared expert (every token, slot 0, one "expert" at w13).
+constexpr int kRowsPerWaveM = 4;
+constexpr int kRowsPerBlockM = kRowsPerWaveM * kWavesPerBlock;
+
+template <int HC, int MT, bool SHARED>
+__global__ __launch_bounds__(kBlock) void k_w13_multi(const f16 *__restrict__ x,
+                                                      const f16 *__restrict__ w13, int M, int I,
+                                                      int K, float *__restrict__ act,
+                                                      const GroupTable *__restrict__ table)
+{
+    constexpr int H = 512 * HC;
+    __shared__ f16x8 xs[MT * HC * kWave];
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int bpe = I / kRowsPerBlockM;
+    const int u = blockIdx.x / bpe;
+    const int j0 = (blockIdx.x % bpe) * kRowsPerBlockM + wave;
 
     int expert;
     unsigned mask;
@@ -428,42 +453,59 @@ __global__ __launch_bounds__(kBlock) void k_w13_silu(const f16 *__restrict__ x,
         mask = (1u << M) - 1u;
 #pragma unroll
         for (int m = 0; m < MT; ++m) slot[m] = 0;
-    } else if (MT == 1) {
-        expert = ids[u];
-        mask = 1u;
-        slot[0] = u;
     } else {
-        const GroupScan<MT> g = group_scan<MT>(ids, M, K);
-        if (blockIdx.x == 0 && wave == 0) group_store<MT>(g, table);
-        if (u >= g.n_u) return; // fewer distinct experts than slots: nothing to do
-        group_pick<MT>(g, u, expert, mask, slot);
+        if (u >= table->n_u) return; // fewer distinct experts than slots: nothing to do
+        expert = table->u_expert[u];
+        mask = table->u_mask[u];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) slot[m] = table->u_slot[u][m];
     }
-
-    // x first (L2-resident, shared by every wave), then the two weight rows
-    f16x8 xv[MT][HC];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        if (mask & (1u << m)) {
-            const f16x8 *xr = reinterpret_cast<const f16x8 *>(x + (size_t)m * H);
-#pragma unroll
-            for (int c = 0; c < HC; ++c) xv[m][c] = xr[c * kWave + lane];
-        }
     const f16 *base = w13 + (size_t)expert * 2 * I * H;
-    const f16x8 *grow = reinterpret_cast<const f16x8 *>(base + (size_t)j * H);
-    const f16x8 *urow = reinterpret_cast<const f16x8 *>(base + (size_t)(I + j) * H);
-    f16x8 wg[HC], wu[HC];
+    f16x8 wg[2][HC], wu[2][HC];
+    auto load_pair = [&](int i, int buf) {
+        const int j = j0 + i * kWavesPerBlock;
+        const f16x8 *grow = reinterpret_cast<const f16x8 *>(base + (size_t)j * H);
+        const f16x8 *urow = reinterpret_cast<const f16x8 *>(base + (size_t)(I + j) * H);
 #pragma unroll
-    for (int c = 0; c < HC; ++c) {
-        wg[c] = stream_load(grow + c * kWave + lane);
-        wu[c] = stream_load(urow + c * kWave + lane);
+        for (int c = 0; c < HC; ++c) {
+            wg[buf][c] = stream_load(grow + c * kWave + lane);
+            wu[buf][c] = stream_load(urow + c * kWave + lane);
+        }
+    };
+    load_pair(0, 0);
+
+    constexpr int kPer = (MT * HC * kWave + kBlock - 1) / kBlock; // 16-byte chunks per thread
+    const int n16 = M * HC * kWave;
+    const f16x8 *x16 = reinterpret_cast<const f16x8 *>(x);
+    f16x8 st[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int q = threadIdx.x + i * kBlock;
+        st[i] = x16[q < n16 ? q : n16 - 1];
     }
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
-        if (mask & (1u << m)) {
-            const float g = row_dot<HC>(wg, xv[m]);
-            const float up = row_dot<HC>(wu, xv[m]);
-            if (lane == 0) act[((size_t)m * K + slot[m]) * I + j] = silu_mul(g, up);
-        }
+    for (int i = 0; i < kPer; ++i) {
+        const int q = threadIdx.x + i * kBlock;
+        if (q < n16) xs[q] = st[i];
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int i = 0; i < kRowsPerWaveM; ++i) {
+        const int buf = i & 1;
+        if (i + 1 < kRowsPerWaveM) load_pair(i + 1, buf ^ 1);
+        const int j = j0 + i * kWavesPerBlock;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (mask & (1u << m)) {
+                f16x8 xv[HC];
+#pragma unroll
+                for (int c = 0; c < HC; ++c) xv[c] = xs[(m * HC + c) * kWave + lane];
+                const float g = row_dot<HC>(wg[buf], xv);
+                const float up = row_dot<HC>(wu[buf], xv);
+                if (lane == 0) act[((size_t)m * K + slot[m]) * I + j] = silu_mul(g, up);
+            }
+    }
 }
 
 // ---------------------------------------------------------------- W2 + combine
@@ -571,6 +613,107 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
     }
 }
 
+
+// ---------------------------------------------------------------- W2 + combine, several tokens
+// The W2 kernel's work and arithmetic for M > 1, with the activations [M, K,
+// I] (or the shared expert's [M, Is]) staged in LDS once per workgroup of
+// kSWaves waves instead of every lane fetching its chunks of every (token,
+// slot) pair from L2 inside the combine loop.  The first batch of W2 rows is
+// requested before the staging loads.
+constexpr int kSWaves = 8;
+constexpr int kSBlock = kSWaves * kWave;
+
+template <int LPR, int CPL, int MT, bool SHARED>
+__global__ __launch_bounds__(kSBlock) void k_w2_staged(
+    const float *__restrict__ act, const f16 *__restrict__ w2, const float *__restrict__ topk_w,
+    const float *__restrict__ shared_in, int M, int H, int I, int K,
+    const GroupTable *__restrict__ table, void *__restrict__ out)
+{
+    extern __shared__ float lds[];
+    constexpr int RPL = kWave / LPR;
+    constexpr int BATCH = 8;
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int r = lane / LPR;
+    const int cl = lane % LPR;
+    const int h = (blockIdx.x * kSWaves + wave) * RPL + r;
+    const int slots = SHARED ? 1 : K;
+    const int n_u = SHARED ? 1 : table->n_u;
+
+    f16x8 wv[BATCH][CPL];
+    auto load_batch = [&](int u0, int cnt) {
+#pragma unroll
+        for (int t = 0; t < BATCH; ++t)
+            if (t < cnt) {
+                const int e = SHARED ? 0 : table->u_expert[u0 + t];
+                const f16x8 *row = reinterpret_cast<const f16x8 *>(w2 + ((size_t)e * H + h) * I);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
+            }
+    };
+    load_batch(0, n_u < BATCH ? n_u : BATCH);
+
+    // stage act: 16-byte chunks, 4 in flight per thread per step
+    const int n4 = M * slots * I / 4;
+    const f32x4 *a4 = reinterpret_cast<const f32x4 *>(act);
+    f32x4 *l4 = reinterpret_cast<f32x4 *>(lds);
+    for (int q0 = 0; q0 < n4; q0 += 4 * kSBlock) {
+        f32x4 st[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = q0 + threadIdx.x + i * kSBlock;
+            st[i] = a4[q < n4 ? q : n4 - 1];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = q0 + threadIdx.x + i * kSBlock;
+            if (q < n4) l4[q] = st[i];
+        }
+    }
+    __syncthreads();
+
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    for (int u0 = 0; u0 < n_u; u0 += BATCH) {
+        const int cnt = n_u - u0 < BATCH ? n_u - u0 : BATCH;
+        if (u0 > 0) load_batch(u0, cnt);
+#pragma unroll
+        for (int t = 0; t < BATCH; ++t)
+            if (t < cnt) {
+                const unsigned mask = SHARED ? (1u << M) - 1u : table->u_mask[u0 + t];
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    if (mask & (1u << m)) {
+                        const int k = SHARED ? 0 : table->u_slot[u0 + t][m];
+                        const float wt = SHARED ? 1.0f : topk_w[(size_t)m * K + k];
+                        const float *a = lds + ((size_t)m * slots + k) * I;
+                        float d = 0.0f;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) {
+                            const f32x4 *ap = reinterpret_cast<const f32x4 *>(a + (c * LPR + cl) * 8);
+                            d = dot8_f32(wv[t][c], ap[0], ap[1], d);
+                        }
+                        acc[m] = fmaf(wt, d, acc[m]);
+                    }
+            }
+    }
+
+    const bool holder = lane == group_holder<LPR>(r);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const float t = group_sum<LPR>(acc[m]);
+        if (m < M && holder) {
+            const size_t o = (size_t)m * H + h;
+            if (SHARED) {
+                static_cast<float *>(out)[o] = t;
+            } else {
+                const float v = shared_in ? t + shared_in[o] : t;
+                static_cast<f16 *>(out)[o] = (f16)v;
+            }
+        }
+    }
+}
 
 // ---------------------------------------------------------------- layer path (M = 1)
 // Three launches for a whole layer at M = 1, plain grids of independent
@@ -799,7 +942,7 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
 }
 
 // ---------------------------------------------------------------- group table only
-// One wave: store U for a W2 stage that runs without the W13 kernel before it.
+// One wave: the group table of an M > 1 call.
 template <int MT>
 __global__ __launch_bounds__(kWave) void k_group_table(const int32_t *__restrict__ ids, int M,
                                                        int K, GroupTable *__restrict__ table)
@@ -895,9 +1038,15 @@ template <int HC, int MT, bool SHARED>
 static hipError_t launch_w13_t(const void *x, const void *w13, const int32_t *ids, int M, int I,
                                int K, int n_slots, float *act, GroupTable *table, hipStream_t s)
 {
-    const int blocks = n_slots * (I / kWavesPerBlock);
-    hipLaunchKernelGGL((k_w13_silu<HC, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
-                       (const f16 *)x, (const f16 *)w13, ids, M, I, K, act, table);
+    if constexpr (MT == 1) {
+        const int blocks = n_slots * (I / kWavesPerBlock);
+        hipLaunchKernelGGL((k_w13_silu<HC, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
+                           (const f16 *)x, (const f16 *)w13, ids, I, act);
+    } else {
+        const int blocks = n_slots * (I / kRowsPerBlockM);
+        hipLaunchKernelGGL((k_w13_multi<HC, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
+                           (const f16 *)x, (const f16 *)w13, M, I, K, act, table);
+    }
     return last();
 }
 
@@ -931,11 +1080,47 @@ static hipError_t launch_w13(const void *x, const void *w13, const int32_t *ids,
     return hipErrorInvalidValue;
 }
 
+constexpr int kMaxDevices = 64;
+
+// Largest dynamic LDS a workgroup may opt into on the current device.
+static size_t lds_optin_bytes()
+{
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess ||
+        v <= 0)
+        return 64 * 1024;
+    return (size_t)v;
+}
+
 template <int LPR, int CPL, int MT, bool SHARED>
 static hipError_t launch_w2_t(const float *act, const void *w2, const int32_t *ids,
                               const float *tw, const float *shared_in, int M, int H, int I, int K,
                               const GroupTable *table, void *out, hipStream_t s)
 {
+    if constexpr (MT > 1) {
+        // several tokens: stage the activations in LDS when they fit
+        const size_t lds = (size_t)M * (SHARED ? 1 : K) * I * sizeof(float);
+        constexpr int rows = (kWave / LPR) * kSWaves;
+        if (H % rows == 0 && lds <= lds_optin_bytes()) {
+            auto kern = k_w2_staged<LPR, CPL, MT, SHARED>;
+            // opt this instance into the device's full LDS, once per device
+            static bool opted[kMaxDevices] = {};
+            int dev = 0;
+            if (lds > 64 * 1024 && hipGetDevice(&dev) == hipSuccess && dev < kMaxDevices &&
+                !opted[dev]) {
+                const hipError_t e = hipFuncSetAttribute(
+                    reinterpret_cast<const void *>(kern),
+                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_optin_bytes());
+                if (e != hipSuccess) return e;
+                opted[dev] = true;
+            }
+            if (lds > 64 * 1024 && dev >= kMaxDevices) return hipErrorInvalidDevice;
+            hipLaunchKernelGGL(kern, dim3(H / rows), dim3(kSBlock), lds, s, act,
+                               (const f16 *)w2, tw, shared_in, M, H, I, K, table, out);
+            return last();
+        }
+    }
     constexpr int rows_per_block = (kWave / LPR) * kWavesPerBlock;
     const int blocks = H / rows_per_block;
     hipLaunchKernelGGL((k_w2_combine<LPR, CPL, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
@@ -982,9 +1167,25 @@ hipError_t launch_shared(const void *x, const void *wgu, const void *wd, int M, 
                            s);
 }
 
+// For M > 1: the distinct selected experts (one wave), read by the W13 and W2 kernels.
+static hipError_t launch_group_table(const int32_t *ids, int M, int K, GroupTable *table,
+                                     hipStream_t s)
+{
+    switch (mt_of(M)) {
+    case 2: hipLaunchKernelGGL(k_group_table<2>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
+    case 4: hipLaunchKernelGGL(k_group_table<4>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
+    default: hipLaunchKernelGGL(k_group_table<8>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
+    }
+    return last();
+}
+
 hipError_t launch_w13_routed(const void *x, const void *w13, const int32_t *ids, int M, int H,
                              int E, int I, int K, float *act, GroupTable *table, hipStream_t s)
 {
+    if (M > 1) {
+        const hipError_t err = launch_group_table(ids, M, K, table, s);
+        if (err != hipSuccess) return err;
+    }
     const int n_slots = M * K < E ? M * K : E;
     return launch_w13<false>(x, w13, ids, M, H, I, K, n_slots, act, table, s);
 }
@@ -1004,12 +1205,7 @@ hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids
 {
     (void)E;
     if (M > 1) {
-        switch (mt_of(M)) {
-        case 2: hipLaunchKernelGGL(k_group_table<2>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
-        case 4: hipLaunchKernelGGL(k_group_table<4>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
-        default: hipLaunchKernelGGL(k_group_table<8>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
-        }
-        const hipError_t err = last();
+        const hipError_t err = launch_group_table(ids, M, K, table, s);
         if (err != hipSuccess) return err;
     }
     return launch_w2<false>(act, w2, ids, tw, shared_in, M, H, I, K, table, y, s);
