@@ -778,11 +778,13 @@ __global__ __launch_bounds__(kBlock) void k_router_shared(const f16 *__restrict_
     }
 }
 
-// Routed workgroups [0, K*I/4): wave 0 selects the experts from the logits
-// (the top-k kernel's arithmetic; workgroup 0 also writes ids and weights),
-// then every wave takes (slot u, row pair j).  Shared workgroups: one wave per
-// RPL = 64/LPR rows of the shared down projection (the W2 kernel's arithmetic
-// with weight 1), s[h] in fp32.
+// Routed workgroups [0, K*I/4) take (slot u, row pair j).  Wave 0 selects
+// from the logits only as far as it needs: u + 1 rounds of the top-k give slot
+// u's expert (the rounds are the top-k kernel's), so the workgroups of early
+// slots start streaming sooner.  The first workgroup of the last slot runs all
+// K rounds and also writes ids and weights (the top-k kernel's arithmetic).
+// Shared workgroups: one wave per RPL = 64/LPR rows of the shared down
+// projection (the W2 kernel's arithmetic with weight 1), s[h] in fp32.
 template <int HC, int NPL, int LPR, int CPL>
 __global__ __launch_bounds__(kBlock) void k_expand(
     const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsd,
@@ -791,21 +793,24 @@ __global__ __launch_bounds__(kBlock) void k_expand(
     float *__restrict__ act, float *__restrict__ s_out)
 {
     constexpr int H = 512 * HC;
-    __shared__ int sh_ids[kMaxTopk];
+    __shared__ int sh_id;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int routed_blocks = K * (I / kWavesPerBlock);
     const int b = blockIdx.x;
     if (b < routed_blocks) {
+        const int per_expert = I / kWavesPerBlock;
+        const int u = b / per_expert;
         if (wave == 0) {
             float v[NPL];
 #pragma unroll
             for (int i = 0; i < NPL; ++i) v[i] = i * kWave + lane < E ? logits[i * kWave + lane] : 0.0f;
+            const bool writer = u == K - 1 && b % per_expert == 0;
             int my_id;
             float my_l;
-            const float lmax = wave_topk_vals<NPL>(v, E, K, my_id, my_l);
-            if (lane < K) sh_ids[lane] = my_id;
-            if (b == 0) {
+            const float lmax = wave_topk_vals<NPL>(v, E, writer ? K : u + 1, my_id, my_l);
+            if (lane == u) sh_id = my_id;
+            if (writer) {
                 const float w = topk_weight_vals<NPL>(v, E, K, renormalize, my_l, lmax);
                 if (lane < K) {
                     ids[lane] = my_id;
@@ -814,10 +819,8 @@ __global__ __launch_bounds__(kBlock) void k_expand(
             }
         }
         __syncthreads();
-        const int per_expert = I / kWavesPerBlock;
-        const int u = b / per_expert;
         const int j = (b % per_expert) * kWavesPerBlock + wave;
-        const float a = w13_pair<HC>(x, w13 + (size_t)sh_ids[u] * 2 * I * H, I, j);
+        const float a = w13_pair<HC>(x, w13 + (size_t)sh_id * 2 * I * H, I, j);
         if (lane == 0) act[(size_t)u * I + j] = a;
     } else {
         constexpr int RPL = kWave / LPR;
