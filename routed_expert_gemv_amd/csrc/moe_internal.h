@@ -15,8 +15,8 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxSlots = kMaxTokens * kMaxTopk; // M*K entries of topk_ids
 constexpr int kMaxInter = 2048;                  // largest I / Is
 
-// Distinct selected experts of an M > 1 call (written by the W13 kernel,
-// read by the W2 kernel of the same call).
+// Distinct selected experts of an M > 1 call (written by the group-table kernel,
+// read by the W13 and W2 kernels of the same call).
 struct GroupTable {
     int n_u;
     int pad_[63];

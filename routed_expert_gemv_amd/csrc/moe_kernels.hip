@@ -101,78 +101,6 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
-// ---------------------------------------------------------------- grouping
-// For M > 1 tokens: the distinct selected experts U, in order of first
-// appearance scanning topk_ids row by row, with the tokens that use each one
-// and the slot k at which each of those tokens selected it.  One wave scans
-// the M*K <= 128 entries: lane i (and i + 64) owns entry i = m*K + k.
-template <int MT>
-struct GroupScan {
-    int v[2];          // expert id of the lane's entries (-1: none)
-    bool first[2];     // first appearance of that id
-    unsigned mask[2];  // tokens that selected that id
-    int slot[2][MT];   // slot k per token (valid where mask is set)
-    int rank[2];       // index of that id in U (valid where first)
-    int n_u;           // |U|
-};
-
-template <int MT>
-__device__ __forceinline__ GroupScan<MT> group_scan(const int32_t *ids, int M, int K)
-{
-    const int lane = lane_id();
-    const int n = M * K;
-    GroupScan<MT> g;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int i = lane + q * kWave;
-        g.v[q] = i < n ? ids[i] : -1;
-        g.first[q] = i < n;
-        g.mask[q] = 0u;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) g.slot[q][m] = 0;
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if (m >= M) break;
-        for (int k = 0; k < K; ++k) {
-            const int j = m * K + k;
-            const int vj = j < kWave ? __builtin_amdgcn_readlane(g.v[0], j)
-                                     : __builtin_amdgcn_readlane(g.v[1], j - kWave);
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                if (vj == g.v[q]) {
-                    if (j < lane + q * kWave) g.first[q] = false;
-                    g.mask[q] |= 1u << m;
-                    g.slot[q][m] = k;
-                }
-        }
-    }
-    const uint64_t b0 = __ballot(g.first[0]);
-    const uint64_t b1 = __ballot(g.first[1]);
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-    g.rank[0] = __popcll(b0 & below);
-    g.rank[1] = __popcll(b0) + __popcll(b1 & below);
-    g.n_u = __popcll(b0) + __popcll(b1);
-    return g;
-}
-
-// Store U (ids, token masks, slots) for the W13 and W2 kernels.
-template <int MT>
-__device__ __forceinline__ void group_store(const GroupScan<MT> &g, GroupTable *table)
-{
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-        if (g.first[q]) {
-            const int r = g.rank[q];
-            table->u_expert[r] = g.v[q];
-            table->u_mask[r] = g.mask[q];
-#pragma unroll
-            for (int m = 0; m < kMaxTokens; ++m)
-                table->u_slot[r][m] = (signed char)(m < MT ? g.slot[q][m < MT ? m : 0] : 0);
-        }
-    if (lane_id() == 0) table->n_u = g.n_u;
-}
-
 // ---------------------------------------------------------------- router GEMV
 // Lane l holds 16-byte chunks c*64 + l of a 2048-wide (H = 512*HC) row.
 template <int HC>
@@ -422,14 +350,14 @@ __global__ __launch_bounds__(kBlock) void k_w13_silu(const f16 *__restrict__ x,
 
 // The same for M > 1 tokens.  The distinct selected experts U (with each
 // one's token mask and slots) come from the group table; a workgroup takes
-// expert u and kRowsPerBlockM row pairs of it, kRowsPerWaveM per wave (rows
-// j0 + i*4, the next pair's loads issued before the current pair's
-// arithmetic).  x [M, H] is staged in LDS once per workgroup; for every token
+// expert u and 4 row pairs per wave (rows j0 + i*4, the next pair's loads
+// issued before the current pair's arithmetic).  x [M, H] is staged in LDS once per workgroup; for every token
 // that routes to the expert: act[m, slot, j] = silu(gate . x_m) * (up . x_m),
 // the single-token arithmetic.
-// SHARED: the shared expert (every token, slot 0, one "expert" at w13).
-constexpr int kRowsPerWaveM = 4;
-constexpr int kRowsPerBlockM = kRowsPerWaveM * kWavesPerBlock;
+// SHARED: the shared expert (every token, slot 0, one "expert" at w13), one
+// row pair per wave so that its single expert still spreads over the chip.
+template <bool SHARED>
+constexpr int rows_per_wave_m() { return SHARED ? 1 : 4; } // the shared expert: more workgroups
 
 template <int HC, int MT, bool SHARED>
 __global__ __launch_bounds__(kBlock) void k_w13_multi(const f16 *__restrict__ x,
@@ -438,6 +366,8 @@ __global__ __launch_bounds__(kBlock) void k_w13_multi(const f16 *__restrict__ x,
                                                       const GroupTable *__restrict__ table)
 {
     constexpr int H = 512 * HC;
+    constexpr int kRowsPerWaveM = rows_per_wave_m<SHARED>();
+    constexpr int kRowsPerBlockM = kRowsPerWaveM * kWavesPerBlock;
     __shared__ f16x8 xs[MT * HC * kWave];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -619,7 +549,8 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
 // I] (or the shared expert's [M, Is]) staged in LDS once per workgroup of
 // kSWaves waves instead of every lane fetching its chunks of every (token,
 // slot) pair from L2 inside the combine loop.  The first batch of W2 rows is
-// requested before the staging loads.
+// requested before the staging loads, and every later batch before the
+// previous one is combined (experts still in order of first appearance).
 constexpr int kSWaves = 8;
 constexpr int kSBlock = kSWaves * kWave;
 
@@ -640,18 +571,21 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     const int slots = SHARED ? 1 : K;
     const int n_u = SHARED ? 1 : table->n_u;
 
-    f16x8 wv[BATCH][CPL];
-    auto load_batch = [&](int u0, int cnt) {
+    // two batches of W2 rows: the next batch is requested before the current
+    // one is combined
+    f16x8 wv[2][BATCH][CPL];
+    auto load_batch = [&](int buf, int u0) {
+        const int cnt = n_u - u0 < BATCH ? n_u - u0 : BATCH;
 #pragma unroll
         for (int t = 0; t < BATCH; ++t)
             if (t < cnt) {
                 const int e = SHARED ? 0 : table->u_expert[u0 + t];
                 const f16x8 *row = reinterpret_cast<const f16x8 *>(w2 + ((size_t)e * H + h) * I);
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
+                for (int c = 0; c < CPL; ++c) wv[buf][t][c] = stream_load(row + c * LPR + cl);
             }
     };
-    load_batch(0, n_u < BATCH ? n_u : BATCH);
+    load_batch(0, 0);
 
     // stage act: 16-byte chunks, 4 in flight per thread per step
     const int n4 = M * slots * I / 4;
@@ -675,9 +609,8 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-    for (int u0 = 0; u0 < n_u; u0 += BATCH) {
+    auto combine = [&](int buf, int u0) {
         const int cnt = n_u - u0 < BATCH ? n_u - u0 : BATCH;
-        if (u0 > 0) load_batch(u0, cnt);
 #pragma unroll
         for (int t = 0; t < BATCH; ++t)
             if (t < cnt) {
@@ -692,11 +625,19 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
 #pragma unroll
                         for (int c = 0; c < CPL; ++c) {
                             const f32x4 *ap = reinterpret_cast<const f32x4 *>(a + (c * LPR + cl) * 8);
-                            d = dot8_f32(wv[t][c], ap[0], ap[1], d);
+                            d = dot8_f32(wv[buf][t][c], ap[0], ap[1], d);
                         }
                         acc[m] = fmaf(wt, d, acc[m]);
                     }
             }
+    };
+    for (int u0 = 0; u0 < n_u; u0 += 2 * BATCH) {
+        if (u0 + BATCH < n_u) load_batch(1, u0 + BATCH);
+        combine(0, u0);
+        if (u0 + BATCH < n_u) {
+            if (u0 + 2 * BATCH < n_u) load_batch(0, u0 + 2 * BATCH);
+            combine(1, u0 + BATCH);
+        }
     }
 
     const bool holder = lane == group_holder<LPR>(r);
@@ -945,13 +886,55 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
 }
 
 // ---------------------------------------------------------------- group table only
-// One wave: the group table of an M > 1 call.
-template <int MT>
-__global__ __launch_bounds__(kWave) void k_group_table(const int32_t *__restrict__ ids, int M,
-                                                       int K, GroupTable *__restrict__ table)
+// ---------------------------------------------------------------- grouping
+// For M > 1 tokens: the distinct selected experts U, in order of first
+// appearance scanning topk_ids row by row, with the tokens that use each one
+// and the slot k at which each of those tokens selected it.  One workgroup,
+// thread i owns entry i = m*K + k (M*K <= 128): per expert, the smallest entry
+// index selecting it (LDS atomic min), the token mask (atomic or) and the
+// slot per token; an entry is a first appearance when it holds that minimum,
+// and its rank in U is the number of first appearances before it.
+constexpr int kGroupThreads = 2 * kWave;
+
+__global__ __launch_bounds__(kGroupThreads) void k_group_table(const int32_t *__restrict__ ids,
+                                                               int M, int K, int E,
+                                                               GroupTable *__restrict__ table)
 {
-    const GroupScan<MT> g = group_scan<MT>(ids, M, K);
-    group_store<MT>(g, table);
+    __shared__ int first_of[kMaxExperts];
+    __shared__ unsigned tokens_of[kMaxExperts];
+    __shared__ signed char slot_of[kMaxExperts][kMaxTokens];
+    __shared__ int n_first0;
+    const int i = threadIdx.x;
+    const int n = M * K;
+    for (int e = i; e < E; e += kGroupThreads) {
+        first_of[e] = 0x7FFFFFFF;
+        tokens_of[e] = 0u;
+#pragma unroll
+        for (int m = 0; m < kMaxTokens; ++m) slot_of[e][m] = 0;
+    }
+    __syncthreads();
+    const int e = i < n ? ids[i] : 0;
+    if (i < n) {
+        const int m = i / K;
+        atomicMin(&first_of[e], i);
+        atomicOr(&tokens_of[e], 1u << m);
+        slot_of[e][m] = (signed char)(i % K);
+    }
+    __syncthreads();
+    const bool first = i < n && first_of[e] == i;
+    const uint64_t b = __ballot(first);
+    const int lane = lane_id();
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+    if (i == 0) n_first0 = __popcll(b);
+    __syncthreads();
+    const int rank = __popcll(b & below) + (i >= kWave ? n_first0 : 0);
+    if (first) {
+        table->u_expert[rank] = e;
+        table->u_mask[rank] = tokens_of[e];
+#pragma unroll
+        for (int m = 0; m < kMaxTokens; ++m) table->u_slot[rank][m] = slot_of[e][m];
+    }
+    if (i == kWave) table->n_u = n_first0 + __popcll(b);
 }
 
 // ---------------------------------------------------------------- probes
@@ -1046,7 +1029,7 @@ static hipError_t launch_w13_t(const void *x, const void *w13, const int32_t *id
         hipLaunchKernelGGL((k_w13_silu<HC, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
                            (const f16 *)x, (const f16 *)w13, ids, I, act);
     } else {
-        const int blocks = n_slots * (I / kRowsPerBlockM);
+        const int blocks = n_slots * (I / (rows_per_wave_m<SHARED>() * kWavesPerBlock));
         hipLaunchKernelGGL((k_w13_multi<HC, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
                            (const f16 *)x, (const f16 *)w13, M, I, K, act, table);
     }
@@ -1170,15 +1153,11 @@ hipError_t launch_shared(const void *x, const void *wgu, const void *wd, int M, 
                            s);
 }
 
-// For M > 1: the distinct selected experts (one wave), read by the W13 and W2 kernels.
-static hipError_t launch_group_table(const int32_t *ids, int M, int K, GroupTable *table,
+// For M > 1: the distinct selected experts, read by the W13 and W2 kernels.
+static hipError_t launch_group_table(const int32_t *ids, int M, int K, int E, GroupTable *table,
                                      hipStream_t s)
 {
-    switch (mt_of(M)) {
-    case 2: hipLaunchKernelGGL(k_group_table<2>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
-    case 4: hipLaunchKernelGGL(k_group_table<4>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
-    default: hipLaunchKernelGGL(k_group_table<8>, dim3(1), dim3(kWave), 0, s, ids, M, K, table); break;
-    }
+    hipLaunchKernelGGL(k_group_table, dim3(1), dim3(kGroupThreads), 0, s, ids, M, K, E, table);
     return last();
 }
 
@@ -1186,7 +1165,7 @@ hipError_t launch_w13_routed(const void *x, const void *w13, const int32_t *ids,
                              int E, int I, int K, float *act, GroupTable *table, hipStream_t s)
 {
     if (M > 1) {
-        const hipError_t err = launch_group_table(ids, M, K, table, s);
+        const hipError_t err = launch_group_table(ids, M, K, E, table, s);
         if (err != hipSuccess) return err;
     }
     const int n_slots = M * K < E ? M * K : E;
@@ -1206,9 +1185,8 @@ hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids
                             const float *shared_in, int M, int H, int E, int I, int K, void *y,
                             GroupTable *table, hipStream_t s)
 {
-    (void)E;
     if (M > 1) {
-        const hipError_t err = launch_group_table(ids, M, K, table, s);
+        const hipError_t err = launch_group_table(ids, M, K, E, table, s);
         if (err != hipSuccess) return err;
     }
     return launch_w2<false>(act, w2, ids, tw, shared_in, M, H, I, K, table, y, s);
