@@ -141,8 +141,12 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
  * For M = 1 (K*I <= 16384) it is three launches: the router rows together
  * with the shared expert's gate/up rows; the routed gate/up rows (each
  * workgroup selecting the experts from the logits itself) together with the
- * shared down rows; the routed down rows with the weighted combine.  Other
- * sizes run the three calls' kernels in sequence.  See moe_layer_launches.
+ * shared down rows; the routed down rows with the weighted combine.  For
+ * M = 2..8 it is four: the router and shared gate/up rows; one workgroup
+ * selecting every token's experts and grouping the distinct ones; their
+ * gate/up rows with the shared down rows; the down rows with the combine.
+ * Other sizes run the three calls' kernels in sequence.  See
+ * moe_layer_launches.
  *   x, w_router, w13, w2  as for moe_route / moe_decode_fused
  *   w_gate_up, w_down     shared expert [2Is, H] / [H, Is], or both NULL (Is ignored)
  *   topk_ids, topk_w, logits  outputs as for moe_route
@@ -155,8 +159,8 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
                             int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
                             float *logits, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Number of kernels moe_layer_decode enqueues for these sizes (3 on the
- * M = 1 path), 0 for unsupported sizes or M = 0. */
+/* Number of kernels moe_layer_decode enqueues for these sizes (3 at M = 1,
+ * 4 at M = 2..8), 0 for unsupported sizes or M = 0. */
 int moe_layer_launches(int M, int H, int E, int I, int K, int Is);
 
 /* ---- test-only probes (not part of the decode path) --------------------- */

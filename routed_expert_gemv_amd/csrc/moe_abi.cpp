@@ -56,13 +56,19 @@ static moe_status layer_decode(const void *x, const void *w_router, const void *
                                       reinterpret_cast<float *>(base + kSharedOutOffset), stage,
                                       stream));
     float *s_out = shared ? reinterpret_cast<float *>(base + kSharedOutOffset) : nullptr;
+    GroupTable *table = reinterpret_cast<GroupTable *>(base + kGroupOffset);
+    if (stage == 0 && lean_m_ok(M, H, E, I, K, Is))
+        return hip_status(launch_lean_m(x, w_router, w13, w2, w_gate_up, w_down, M, H, E, I, K,
+                                        Is, renormalize, topk_ids, topk_w, logits, y, act, act_s,
+                                        reinterpret_cast<float *>(base + kSharedOutOffset),
+                                        table, stream));
     hipError_t err = hipSuccess;
     if (shared) err = launch_shared(x, w_gate_up, w_down, M, H, Is, s_out, act_s, stream);
     if (err == hipSuccess)
         err = launch_route(x, w_router, M, H, E, K, renormalize, topk_ids, topk_w, logits, stream);
     if (err == hipSuccess)
-        err = launch_fused(x, w13, w2, topk_ids, topk_w, s_out, M, H, E, I, K, y, act,
-                           reinterpret_cast<GroupTable *>(base + kGroupOffset), stream);
+        err = launch_fused(x, w13, w2, topk_ids, topk_w, s_out, M, H, E, I, K, y, act, table,
+                           stream);
     return hip_status(err);
 }
 
@@ -158,6 +164,7 @@ int moe_layer_launches(int M, int H, int E, int I, int K, int Is)
     if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (Is != 0 && !i_ok(Is))) return 0;
     if (M == 0) return 0;
     if (lean_ok(M, H, E, I, K, Is)) return 3;
+    if (lean_m_ok(M, H, E, I, K, Is)) return 4;
     // shared_expert (2) + moe_route (2) + moe_decode_fused (2)
     return (Is ? 2 : 0) + 2 + 2;
 }

@@ -57,6 +57,13 @@ hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream
 hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s);
 // The layer at M = 1 in three launches (router + shared gate/up, expand, reduce);
 // stage 0 runs all three, stage 1..3 that launch alone.
+// The layer for 2..8 tokens in four launches (router + shared gate/up, the
+// selection with the group table, expand, the staged W2 kernel).
+bool lean_m_ok(int M, int H, int E, int I, int K, int Is);
+hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const void *w2,
+                         const void *wsgu, const void *wsd, int M, int H, int E, int I, int K,
+                         int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
+                         float *act, float *act_s, float *s_out, GroupTable *table, hipStream_t s);
 bool lean_ok(int M, int H, int E, int I, int K, int Is);
 hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,

@@ -129,14 +129,13 @@ __device__ __forceinline__ float row_dot(const f16x8 (&w)[HC], const f16x8 (&xv)
     return wave_sum(acc);
 }
 
-// One wave per expert row e: logits[m, e] = sum_h Wr[e, h] x[m, h].
+// One wave, expert row e: logits[m, e] = sum_h Wr[e, h] x[m, h] for m < M.
 template <int HC>
-__global__ __launch_bounds__(kWave) void k_router(const f16 *__restrict__ x,
-                                                  const f16 *__restrict__ wr, int M, int E,
-                                                  float *__restrict__ logits)
+__device__ __forceinline__ void router_row(const f16 *__restrict__ x,
+                                           const f16 *__restrict__ wr, int M, int E, int e,
+                                           float *__restrict__ logits)
 {
     constexpr int H = 512 * HC;
-    const int e = blockIdx.x;
     f16x8 w[HC];
     load_row<HC>(wr + (size_t)e * H, w);
     for (int m = 0; m < M; ++m) {
@@ -145,6 +144,14 @@ __global__ __launch_bounds__(kWave) void k_router(const f16 *__restrict__ x,
         const float t = row_dot<HC>(w, xv);
         if (lane_id() == 0) logits[(size_t)m * E + e] = t;
     }
+}
+
+template <int HC>
+__global__ __launch_bounds__(kWave) void k_router(const f16 *__restrict__ x,
+                                                  const f16 *__restrict__ wr, int M, int E,
+                                                  float *__restrict__ logits)
+{
+    router_row<HC>(x, wr, M, E, blockIdx.x, logits);
 }
 
 // ---------------------------------------------------------------- top-k + softmax
@@ -359,21 +366,22 @@ __global__ __launch_bounds__(kBlock) void k_w13_silu(const f16 *__restrict__ x,
 template <bool SHARED>
 constexpr int rows_per_wave_m() { return SHARED ? 1 : 4; } // the shared expert: more workgroups
 
+// Workgroup b of the multi-token W13 work (xs: LDS for x, MT*HC*64 chunks).
 template <int HC, int MT, bool SHARED>
-__global__ __launch_bounds__(kBlock) void k_w13_multi(const f16 *__restrict__ x,
-                                                      const f16 *__restrict__ w13, int M, int I,
-                                                      int K, float *__restrict__ act,
-                                                      const GroupTable *__restrict__ table)
+__device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
+                                                const f16 *__restrict__ w13, int M, int I, int K,
+                                                float *__restrict__ act,
+                                                const GroupTable *__restrict__ table, int b,
+                                                f16x8 *xs)
 {
     constexpr int H = 512 * HC;
     constexpr int kRowsPerWaveM = rows_per_wave_m<SHARED>();
     constexpr int kRowsPerBlockM = kRowsPerWaveM * kWavesPerBlock;
-    __shared__ f16x8 xs[MT * HC * kWave];
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int bpe = I / kRowsPerBlockM;
-    const int u = blockIdx.x / bpe;
-    const int j0 = (blockIdx.x % bpe) * kRowsPerBlockM + wave;
+    const int u = b / bpe;
+    const int j0 = (b % bpe) * kRowsPerBlockM + wave;
 
     int expert;
     unsigned mask;
@@ -436,6 +444,16 @@ __global__ __launch_bounds__(kBlock) void k_w13_multi(const f16 *__restrict__ x,
                 if (lane == 0) act[((size_t)m * K + slot[m]) * I + j] = silu_mul(g, up);
             }
     }
+}
+
+template <int HC, int MT, bool SHARED>
+__global__ __launch_bounds__(kBlock) void k_w13_multi(const f16 *__restrict__ x,
+                                                      const f16 *__restrict__ w13, int M, int I,
+                                                      int K, float *__restrict__ act,
+                                                      const GroupTable *__restrict__ table)
+{
+    __shared__ f16x8 xs[MT * HC * kWave];
+    w13_multi_block<HC, MT, SHARED>(x, w13, M, I, K, act, table, blockIdx.x, xs);
 }
 
 // ---------------------------------------------------------------- W2 + combine
@@ -562,7 +580,7 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
 {
     extern __shared__ float lds[];
     constexpr int RPL = kWave / LPR;
-    constexpr int BATCH = 8;
+    constexpr int BATCH = 8 / CPL; // 16-byte W2 chunks per lane per buffer: 8
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int r = lane / LPR;
@@ -885,56 +903,170 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
     if (lane == group_holder<LPR>(r)) y[h] = (f16)(s_in ? t + s_h : t);
 }
 
-// ---------------------------------------------------------------- group table only
 // ---------------------------------------------------------------- grouping
 // For M > 1 tokens: the distinct selected experts U, in order of first
 // appearance scanning topk_ids row by row, with the tokens that use each one
-// and the slot k at which each of those tokens selected it.  One workgroup,
-// thread i owns entry i = m*K + k (M*K <= 128): per expert, the smallest entry
-// index selecting it (LDS atomic min), the token mask (atomic or) and the
-// slot per token; an entry is a first appearance when it holds that minimum,
-// and its rank in U is the number of first appearances before it.
+// and the slot k at which each of those tokens selected it.  Threads
+// [0, kGroupThreads) of a workgroup, thread i owning entry i = m*K + k (M*K <=
+// 128): per expert, the smallest entry index selecting it (LDS atomic min),
+// the token mask (atomic or) and the slot per token; an entry is a first
+// appearance when it holds that minimum, and its rank in U is the number of
+// first appearances before it.  Every thread of the workgroup must call it.
 constexpr int kGroupThreads = 2 * kWave;
+
+struct GroupScratch {
+    int first_of[kMaxExperts];
+    unsigned tokens_of[kMaxExperts];
+    signed char slot_of[kMaxExperts][kMaxTokens];
+    int n_first0;
+};
+
+__device__ __forceinline__ void build_group_table(const int32_t *ids, int M, int K, int E,
+                                                  GroupTable *__restrict__ table,
+                                                  GroupScratch &g)
+{
+    const int i = threadIdx.x;
+    const int n = M * K;
+    for (int e = i; e < E; e += blockDim.x) {
+        g.first_of[e] = 0x7FFFFFFF;
+        g.tokens_of[e] = 0u;
+#pragma unroll
+        for (int m = 0; m < kMaxTokens; ++m) g.slot_of[e][m] = 0;
+    }
+    __syncthreads();
+    const bool mine = i < kGroupThreads && i < n;
+    const int e = mine ? ids[i] : 0;
+    if (mine) {
+        const int m = i / K;
+        atomicMin(&g.first_of[e], i);
+        atomicOr(&g.tokens_of[e], 1u << m);
+        g.slot_of[e][m] = (signed char)(i % K);
+    }
+    __syncthreads();
+    const bool first = mine && g.first_of[e] == i;
+    const uint64_t b = __ballot(first);
+    const int lane = lane_id();
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+    if (i == 0) g.n_first0 = __popcll(b);
+    __syncthreads();
+    const int rank = __popcll(b & below) + (i >= kWave ? g.n_first0 : 0);
+    if (first) {
+        table->u_expert[rank] = e;
+        table->u_mask[rank] = g.tokens_of[e];
+#pragma unroll
+        for (int m = 0; m < kMaxTokens; ++m) table->u_slot[rank][m] = g.slot_of[e][m];
+    }
+    if (i == kWave) table->n_u = g.n_first0 + __popcll(b);
+}
 
 __global__ __launch_bounds__(kGroupThreads) void k_group_table(const int32_t *__restrict__ ids,
                                                                int M, int K, int E,
                                                                GroupTable *__restrict__ table)
 {
-    __shared__ int first_of[kMaxExperts];
-    __shared__ unsigned tokens_of[kMaxExperts];
-    __shared__ signed char slot_of[kMaxExperts][kMaxTokens];
-    __shared__ int n_first0;
-    const int i = threadIdx.x;
-    const int n = M * K;
-    for (int e = i; e < E; e += kGroupThreads) {
-        first_of[e] = 0x7FFFFFFF;
-        tokens_of[e] = 0u;
-#pragma unroll
-        for (int m = 0; m < kMaxTokens; ++m) slot_of[e][m] = 0;
+    __shared__ GroupScratch g;
+    build_group_table(ids, M, K, E, table, g);
+}
+
+// ---------------------------------------------------------------- layer path (M > 1)
+// Four launches for a whole layer with 2..8 tokens, the multi-token kernels'
+// arithmetic throughout (so the results equal the three calls bit for bit):
+//   k_route_shared_m  router rows for every token; shared gate/up row pairs
+//   k_select_m        one workgroup: every token's top-k, then the group table
+//   k_expand_m        routed gate/up rows of the distinct experts; shared down
+//   (the staged W2 kernel with the shared output added)
+
+template <int HC, int MT>
+__global__ __launch_bounds__(kBlock) void k_route_shared_m(const f16 *__restrict__ x,
+                                                           const f16 *__restrict__ wr,
+                                                           const f16 *__restrict__ wsgu, int M,
+                                                           int E, int Is,
+                                                           float *__restrict__ logits,
+                                                           float *__restrict__ act_s)
+{
+    __shared__ f16x8 xs[MT * HC * kWave];
+    const int router_blocks = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+    if ((int)blockIdx.x < router_blocks) {
+        const int e = blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+        if (e < E) router_row<HC>(x, wr, M, E, e, logits);
+        return;
     }
-    __syncthreads();
-    const int e = i < n ? ids[i] : 0;
-    if (i < n) {
-        const int m = i / K;
-        atomicMin(&first_of[e], i);
-        atomicOr(&tokens_of[e], 1u << m);
-        slot_of[e][m] = (signed char)(i % K);
-    }
-    __syncthreads();
-    const bool first = i < n && first_of[e] == i;
-    const uint64_t b = __ballot(first);
+    w13_multi_block<HC, MT, true>(x, wsgu, M, Is, 1, act_s, nullptr, blockIdx.x - router_blocks,
+                                  xs);
+}
+
+template <int NPL>
+__global__ __launch_bounds__(kBlock) void k_select_m(const float *__restrict__ logits, int M,
+                                                     int E, int K, int renormalize,
+                                                     int32_t *__restrict__ ids,
+                                                     float *__restrict__ weights,
+                                                     GroupTable *__restrict__ table)
+{
+    __shared__ GroupScratch g;
+    __shared__ int32_t sids[kMaxSlots];
+    const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
-    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-    if (i == 0) n_first0 = __popcll(b);
-    __syncthreads();
-    const int rank = __popcll(b & below) + (i >= kWave ? n_first0 : 0);
-    if (first) {
-        table->u_expert[rank] = e;
-        table->u_mask[rank] = tokens_of[e];
+    for (int m = wave; m < M; m += kWavesPerBlock) { // the top-k kernel's work, token m
+        const float *L = logits + (size_t)m * E;
+        float v[NPL];
 #pragma unroll
-        for (int m = 0; m < kMaxTokens; ++m) table->u_slot[rank][m] = slot_of[e][m];
+        for (int i = 0; i < NPL; ++i) v[i] = i * kWave + lane < E ? L[i * kWave + lane] : 0.0f;
+        int my_id;
+        float my_l;
+        const float lmax = wave_topk_vals<NPL>(v, E, K, my_id, my_l);
+        const float w = topk_weight_vals<NPL>(v, E, K, renormalize, my_l, lmax);
+        if (lane < K) {
+            ids[(size_t)m * K + lane] = my_id;
+            weights[(size_t)m * K + lane] = w;
+            sids[m * K + lane] = my_id;
+        }
     }
-    if (i == kWave) table->n_u = n_first0 + __popcll(b);
+    __syncthreads();
+    build_group_table(sids, M, K, E, table, g);
+}
+
+// Routed workgroups: the multi-token W13 work.  Shared workgroups: RPL = 64/LPR
+// rows of the shared down projection per wave for every token (the W2
+// kernel's arithmetic with weight 1), s[m, h] in fp32.
+template <int HC, int MT, int LPR, int CPL>
+__global__ __launch_bounds__(kBlock) void k_expand_m(const f16 *__restrict__ x,
+                                                     const f16 *__restrict__ w13,
+                                                     const f16 *__restrict__ wsd,
+                                                     const float *__restrict__ act_s, int M, int H,
+                                                     int I, int K, int Is, int routed_blocks,
+                                                     float *__restrict__ act,
+                                                     float *__restrict__ s_out,
+                                                     const GroupTable *__restrict__ table)
+{
+    __shared__ f16x8 xs[MT * HC * kWave];
+    const int b = blockIdx.x;
+    if (b < routed_blocks) {
+        w13_multi_block<HC, MT, false>(x, w13, M, I, K, act, table, b, xs);
+        return;
+    }
+    constexpr int RPL = kWave / LPR;
+    const int lane = lane_id();
+    const int r = lane / LPR;
+    const int cl = lane % LPR;
+    const int h = ((b - routed_blocks) * kWavesPerBlock + threadIdx.x / kWave) * RPL + r;
+    const f16x8 *row = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * Is);
+    f16x8 wv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) wv[c] = stream_load(row + c * LPR + cl);
+    const bool holder = lane == group_holder<LPR>(r);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float d = 0.0f;
+        if (m < M) {
+            const float *am = act_s + (size_t)m * Is;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const f32x4 *ap = reinterpret_cast<const f32x4 *>(am + (c * LPR + cl) * 8);
+                d = dot8_f32(wv[c], ap[0], ap[1], d);
+            }
+        }
+        const float t = group_sum<LPR>(fmaf(1.0f, d, 0.0f));
+        if (m < M && holder) s_out[(size_t)m * H + h] = t;
+    }
 }
 
 // ---------------------------------------------------------------- probes
@@ -1314,6 +1446,98 @@ static hipError_t launch_reduce_t(const float *act, const void *w2, const int32_
     else
         hipLaunchKernelGGL((k_reduce<LPR, CPL, 8>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
     return last();
+}
+
+bool lean_m_ok(int M, int H, int E, int I, int K, int Is)
+{
+    (void)E;
+    (void)I;
+    (void)K;
+    return M >= 2 && M <= kMaxTokens && (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
+}
+
+template <int HC, int MT, int LPR, int CPL>
+static hipError_t launch_expand_m_t(const void *x, const void *w13, const void *wsd,
+                                    const float *act_s, int M, int I, int K, int Is, int n_slots,
+                                    float *act, float *s_out, const GroupTable *table, hipStream_t s)
+{
+    constexpr int H = 512 * HC;
+    const int routed = n_slots * (I / (rows_per_wave_m<false>() * kWavesPerBlock));
+    const int shared = Is ? H / (kWavesPerBlock * (kWave / LPR)) : 0;
+    hipLaunchKernelGGL((k_expand_m<HC, MT, LPR, CPL>), dim3(routed + shared), dim3(kBlock), 0, s,
+                       (const f16 *)x, (const f16 *)w13, (const f16 *)wsd, act_s, M, H, I, K, Is,
+                       routed, act, s_out, table);
+    return last();
+}
+
+template <int HC, int MT>
+static hipError_t launch_lean_m_t(const void *x, const void *wr, const void *w13,
+                                  const void *wsgu, const void *wsd, int M, int E, int I, int K,
+                                  int Is, int renorm, int32_t *ids, float *w, float *logits,
+                                  float *act, float *act_s, float *s_out, GroupTable *table,
+                                  hipStream_t s)
+{
+    const int rb = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL((k_route_shared_m<HC, MT>), dim3(rb + Is / kWavesPerBlock), dim3(kBlock),
+                       0, s, (const f16 *)x, (const f16 *)wr, (const f16 *)wsgu, M, E, Is, logits,
+                       act_s);
+    hipError_t err = last();
+    if (err != hipSuccess) return err;
+    if (E <= kWave)
+        hipLaunchKernelGGL(k_select_m<1>, dim3(1), dim3(kBlock), 0, s, logits, M, E, K, renorm,
+                           ids, w, table);
+    else if (E <= 4 * kWave)
+        hipLaunchKernelGGL(k_select_m<4>, dim3(1), dim3(kBlock), 0, s, logits, M, E, K, renorm,
+                           ids, w, table);
+    else
+        hipLaunchKernelGGL(k_select_m<kMaxExperts / kWave>, dim3(1), dim3(kBlock), 0, s, logits,
+                           M, E, K, renorm, ids, w, table);
+    if ((err = last()) != hipSuccess) return err;
+    const int n_slots = M * K < E ? M * K : E;
+    switch (Is) {
+    case 0:
+    case 512: return launch_expand_m_t<HC, MT, 64, 1>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
+    case 64: return launch_expand_m_t<HC, MT, 8, 1>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
+    case 128: return launch_expand_m_t<HC, MT, 16, 1>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
+    case 256: return launch_expand_m_t<HC, MT, 32, 1>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
+    case 1024: return launch_expand_m_t<HC, MT, 64, 2>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
+    default: return launch_expand_m_t<HC, MT, 64, 4>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
+    }
+}
+
+template <int HC>
+static hipError_t launch_lean_m_hc(const void *x, const void *wr, const void *w13,
+                                   const void *wsgu, const void *wsd, int M, int E, int I, int K,
+                                   int Is, int renorm, int32_t *ids, float *w, float *logits,
+                                   float *act, float *act_s, float *s_out, GroupTable *table,
+                                   hipStream_t s)
+{
+    switch (mt_of(M)) {
+    case 2: return launch_lean_m_t<HC, 2>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s);
+    case 4: return launch_lean_m_t<HC, 4>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s);
+    case 8:
+        if constexpr (HC <= 4)
+            return launch_lean_m_t<HC, 8>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s);
+        return hipErrorInvalidValue;
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const void *w2,
+                         const void *wsgu, const void *wsd, int M, int H, int E, int I, int K,
+                         int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
+                         float *act, float *act_s, float *s_out, GroupTable *table, hipStream_t s)
+{
+    hipError_t err;
+    switch (H / 512) {
+    case 1: err = launch_lean_m_hc<1>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s); break;
+    case 2: err = launch_lean_m_hc<2>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s); break;
+    case 4: err = launch_lean_m_hc<4>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s); break;
+    case 8: err = launch_lean_m_hc<8>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (err != hipSuccess) return err;
+    return launch_w2<false>(act, w2, ids, w, Is ? s_out : nullptr, M, H, I, K, table, y, s);
 }
 
 hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
