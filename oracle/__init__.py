@@ -61,6 +61,8 @@ def _load():
             lib.oracle_router_logits.argtypes = [_DP, _DP, C.c_int, C.c_int, C.c_int, _DP]
             lib.oracle_topk_softmax.argtypes = [_DP, C.c_int, C.c_int, C.c_int, _IP, _DP, _DP]
             lib.oracle_topk_softmax.restype = C.c_int
+            lib.oracle_route_weights.argtypes = [_DP, C.c_int, C.c_int, _IP, C.c_int, _DP]
+            lib.oracle_route_weights.restype = C.c_int
             lib.oracle_expert_activated.argtypes = [_DP, _DP, C.c_int, C.c_int, C.c_int, _DP]
             lib.oracle_weighted_down.argtypes = [C.POINTER(_DP), _DP, _DP, C.c_int, C.c_int,
                                                  C.c_int, C.c_int, _DP]
@@ -131,6 +133,29 @@ def topk_softmax(logits, K: int, renormalize: bool = True):
         ids[m], w[m], margin[m] = idr, wr_, mg[0]
     shp = lg.shape[:-1]
     return ids.reshape(shp + (K,)), w.reshape(shp + (K,)), margin.reshape(shp)
+
+
+def route_weights(logits, ids, renormalize: bool = True) -> np.ndarray:
+    """Routing weights of a given selection ids [.., K] under logits [.., E] (fp64)."""
+    lib = _load()
+    lg = _f64(logits)
+    E = lg.shape[-1]
+    l2 = lg.reshape(-1, E)
+    idv = np.ascontiguousarray(ids, dtype=np.int32)
+    K = idv.shape[-1]
+    i2 = idv.reshape(-1, K)
+    assert i2.shape[0] == l2.shape[0]
+    w = np.empty((l2.shape[0], K), dtype=np.float64)
+    for m in range(l2.shape[0]):
+        row = np.ascontiguousarray(l2[m])
+        idr = np.ascontiguousarray(i2[m])
+        wr_ = np.empty(K, dtype=np.float64)
+        rc = lib.oracle_route_weights(_p(row), E, K, idr.ctypes.data_as(_IP),
+                                      int(bool(renormalize)), _p(wr_))
+        if rc != 0:
+            raise ValueError("oracle_route_weights: bad sizes or ids (E=%d K=%d)" % (E, K))
+        w[m] = wr_
+    return w.reshape(idv.shape)
 
 
 def expert_activated(x, w13e, nthreads: int = 1) -> np.ndarray:

@@ -135,6 +135,34 @@ int oracle_topk_softmax(const double *logits, int E, int K, int renormalize,
     return 0;
 }
 
+/* [W] part 8: the routing weights of a given selection.  For expert ids
+ * ids[0..K) (each in [0, E)), weights[k] = softmax over all E logits taken at
+ * ids[k], divided by their sum over the K entries when renormalize != 0.
+ * Used where the selection itself is not unique (logits closer than their
+ * rounding error): any top-K order of the computed logits is a correct
+ * routing, and this gives the exact weights that routing carries.
+ * Returns 0, or -1 on bad sizes or an id outside [0, E). */
+int oracle_route_weights(const double *logits, int E, int K, const int32_t *ids,
+                         int renormalize, double *weights)
+{
+    if (E <= 0 || K <= 0 || K > E) return -1;
+    for (int k = 0; k < K; ++k)
+        if (ids[k] < 0 || ids[k] >= E) return -1;
+    double lmax = logits[0];
+    for (int e = 1; e < E; ++e)
+        if (logits[e] > lmax) lmax = logits[e];
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) z += exp(logits[e] - lmax);
+    double picked = 0.0; /* sum of the given ids' probabilities */
+    for (int k = 0; k < K; ++k) {
+        weights[k] = exp(logits[ids[k]] - lmax) / z;
+        picked += weights[k];
+    }
+    if (renormalize != 0)
+        for (int k = 0; k < K; ++k) weights[k] /= picked;
+    return 0;
+}
+
 static double silu(double g) { return g / (1.0 + exp(-g)); }
 
 /* [W] part 10 (W13 kernel) + part 3 (SiluAndMul), for one expert and one token.

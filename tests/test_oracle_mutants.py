@@ -38,6 +38,9 @@ MUTANTS = [
      "oracle_expert_activated(x, w13sel,"),
     ("up_half_offset_wrong", "const double *urow = w13e + (size_t)(I + j) * H;",
      "const double *urow = w13e + (size_t)(I + j - 1) * H;"),
+    ("route_weights_ignore_ids", "weights[k] = exp(logits[ids[k]] - lmax) / z;",
+     "weights[k] = exp(logits[k] - lmax) / z;"),
+    ("route_weights_not_renormalised", "if (renormalize != 0)\n", "if (0)\n"),
 ]
 
 

@@ -303,3 +303,51 @@ def test_tokens_are_routed_independently():
         one = oracle.moe_layer(t["x"][m:m + 1], t["wr"], t["w13"], t["w2"], K=4)
         np.testing.assert_array_equal(one["y"][0], allm["y"][m])
         np.testing.assert_array_equal(one["expert_ids"][0], allm["expert_ids"][m])
+
+
+# ---- routing weights of a given selection (used where the selection has ties
+# within rounding: BI-V100 worklog, part 8 -- the routing step is top-k + softmax)
+
+def test_route_weights_two_experts_are_logistic():
+    # renormalised weights of two experts depend only on their logit gap:
+    # w_i = 1 / (1 + exp(L_j - L_i))
+    lg = np.array([0.25, -1.5, 2.0, 0.75, -0.5])
+    w = oracle.route_weights(lg, np.array([3, 1]), True)
+    assert w[0] == pytest.approx(1.0 / (1.0 + math.exp(-1.5 - 0.75)), rel=1e-14)
+    assert w[1] == pytest.approx(1.0 / (1.0 + math.exp(0.75 + 1.5)), rel=1e-14)
+
+
+def test_route_weights_uniform_logits():
+    E, K = 12, 5
+    lg = np.full(E, 0.3)
+    ids = np.array([7, 0, 11, 2, 5])
+    np.testing.assert_allclose(oracle.route_weights(lg, ids, True), np.full(K, 1.0 / K), rtol=1e-15)
+    np.testing.assert_allclose(oracle.route_weights(lg, ids, False), np.full(K, 1.0 / E), rtol=1e-15)
+
+
+def test_route_weights_follow_the_ids_order():
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal(32)
+    ids = np.array([4, 17, 9, 30])
+    w = oracle.route_weights(lg, ids, False)
+    perm = np.array([2, 0, 3, 1])
+    np.testing.assert_array_equal(oracle.route_weights(lg, ids[perm], False), w[perm])
+    # unnormalised weights of every expert are the full softmax (sum 1, ratios exp(dL))
+    full = oracle.route_weights(lg, np.arange(32), False)
+    assert full.sum() == pytest.approx(1.0, abs=1e-14)
+    assert full[4] / full[17] == pytest.approx(math.exp(lg[4] - lg[17]), rel=1e-13)
+
+
+def test_route_weights_of_the_top_k_match_topk_softmax():
+    rng = np.random.default_rng(6)
+    lg = rng.standard_normal((3, 64))
+    for renorm in (True, False):
+        ids, w, _ = oracle.topk_softmax(lg, 6, renorm)
+        np.testing.assert_allclose(oracle.route_weights(lg, ids, renorm), w, rtol=1e-14)
+
+
+def test_route_weights_reject_bad_ids():
+    with pytest.raises(ValueError):
+        oracle.route_weights(np.zeros(4), np.array([0, 4]), True)
+    with pytest.raises(ValueError):
+        oracle.route_weights(np.zeros(4), np.array([-1, 2]), True)
