@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 #define MOE_MAX_TOKENS 8
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_EXPERTS 1024

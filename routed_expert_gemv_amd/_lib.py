@@ -1,4 +1,5 @@
-"""ctypes loader of libmoe_decode.so and the prototypes of include/moe_decode.h."""
+"""ctypes loader of libmoe_decode.so and the prototypes of include/moe_decode.h and
+include/moe_prefill.h."""
 from __future__ import annotations
 
 import ctypes as C
@@ -16,7 +17,8 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
 EXPORTED = ["moe_abi_version", "moe_status_str", "moe_workspace_bytes", "moe_route",
             "shared_expert", "moe_decode_fused", "moe_dbg_wave_sum", "moe_dbg_w13_silu",
             "moe_dbg_w2_combine", "moe_layer_decode", "moe_layer_launches", "moe_dbg_layer_stage",
-            "moe_probe_empty", "moe_probe_read", "moe_probe_copy"]
+            "moe_probe_empty", "moe_probe_read", "moe_probe_copy", "moe_prefill_workspace_bytes",
+            "moe_layer_prefill", "moe_dbg_prefill_stage"]
 
 _vp = C.c_void_p
 _i = C.c_int
@@ -65,6 +67,12 @@ def lib() -> C.CDLL:
             L.moe_probe_read.argtypes = [_vp, _sz, _vp, _vp]
             L.moe_layer_launches.restype = _i
             L.moe_layer_launches.argtypes = [_i] * 6
+            L.moe_prefill_workspace_bytes.restype = _sz
+            L.moe_prefill_workspace_bytes.argtypes = [_i] * 6
+            L.moe_layer_prefill.restype = _i
+            L.moe_layer_prefill.argtypes = L.moe_layer_decode.argtypes
+            L.moe_dbg_prefill_stage.restype = _i
+            L.moe_dbg_prefill_stage.argtypes = [_i] + L.moe_layer_decode.argtypes
             _lib = L
     return _lib
 

@@ -207,8 +207,8 @@ def moe_dbg_w2_combine(activated, w2, topk_ids, topk_w, shared_in=None, y=None, 
 
 
 def _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids, topk_w,
-                logits, y, ws):
-    """Checks and marshals moe_layer_decode's arguments; returns (outputs, C args)."""
+                logits, y, ws, make_ws=None):
+    """Checks and marshals the layer entry points' arguments; returns (outputs, C args)."""
     _dev_tensor("x", x, torch.float16, 2)
     _dev_tensor("w_router", w_router, torch.float16, 2)
     _dev_tensor("w13", w13, torch.float16, 3)
@@ -239,7 +239,7 @@ def _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_id
         if t.numel() != n:
             raise ValueError("%s must have %d elements" % (name, n))
     if ws is None:
-        ws = workspace(max(M, 1), H, E, I, K, Is, dev)
+        ws = (make_ws or workspace)(max(M, 1), H, E, I, K, Is, dev)
     _dev_tensor("ws", ws, torch.uint8)
     args = (_ptr(x), _ptr(w_router), _ptr(w13), _ptr(w2), _ptr(w_gate_up), _ptr(w_down), M, H, E,
             I, K, Is, int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
@@ -302,4 +302,39 @@ def moe_probe_read(buf, out=None, stream=None):
     n = buf.numel() * buf.element_size()
     _check("moe_probe_read", _lib.lib().moe_probe_read(_ptr(buf), n - n % 16, _ptr(out),
                                                        _stream(stream, buf.device)))
+    return out
+
+
+def moe_prefill_workspace_bytes(T: int, H: int, E: int, I: int, K: int, Is: int = 0) -> int:
+    return int(_lib.lib().moe_prefill_workspace_bytes(T, H, E, I, K, Is))
+
+
+def prefill_workspace(T: int, H: int, E: int, I: int, K: int, Is: int = 0,
+                      device=None) -> torch.Tensor:
+    """A device workspace big enough for moe_layer_prefill at these sizes."""
+    n = moe_prefill_workspace_bytes(T, H, E, I, K, Is)
+    if n == 0:
+        raise MoeError("moe_prefill_workspace_bytes", -2)
+    return torch.zeros(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
+
+
+def moe_layer_prefill(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int = 8,
+                      renormalize: bool = True, topk_ids=None, topk_w=None, logits=None, y=None,
+                      ws=None, stream=None):
+    """The layer for T tokens at once (x [T, H]) on the matrix cores.
+    Returns (y, topk_ids, topk_w, logits)."""
+    out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
+                            topk_w, logits, y, ws, prefill_workspace)
+    _check("moe_layer_prefill", _lib.lib().moe_layer_prefill(*args, _stream(stream, x.device)))
+    return out
+
+
+def moe_dbg_prefill_stage(stage: int, x, w_router, w13, w2, w_gate_up=None, w_down=None,
+                          K: int = 8, renormalize: bool = True, topk_ids=None, topk_w=None,
+                          logits=None, y=None, ws=None, stream=None):
+    """One of moe_layer_prefill's six launches alone (test-only; for timing)."""
+    out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
+                            topk_w, logits, y, ws, prefill_workspace)
+    _check("moe_dbg_prefill_stage",
+           _lib.lib().moe_dbg_prefill_stage(int(stage), *args, _stream(stream, x.device)))
     return out

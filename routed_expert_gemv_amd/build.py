@@ -10,8 +10,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_decode.so")
-SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_abi.cpp")]
-HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(INCLUDE, "moe_decode.h")]
+SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_prefill.hip"),
+           os.path.join(CSRC, "moe_abi.cpp")]
+HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(INCLUDE, "moe_decode.h"),
+           os.path.join(INCLUDE, "moe_prefill.h")]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for every HIP file of this library.
 HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",

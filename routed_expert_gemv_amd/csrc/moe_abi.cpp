@@ -3,6 +3,7 @@
 // kernel launches on the caller's stream.  Every check runs before anything is
 // enqueued; nothing here allocates, synchronises or reads device memory.
 #include "moe_decode.h"
+#include "moe_prefill.h"
 
 #include "moe_internal.h"
 
@@ -24,7 +25,40 @@ size_t routed_ws_bytes(int M, int I, int K)
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+bool pf_dim_ok(int n, int hi) { return n >= 64 && n <= hi && n % 64 == 0; }
+// The grouped GEMMs address token rows with 32-bit byte offsets: the routed
+// activations [T*K, I] fp16 must stay below 4 GiB (x and the shared
+// activations always do at these bounds).
+bool pf_shape_ok(int T, int H, int E, int I, int K, int Is)
+{
+    return T >= 0 && T <= 65536 && pf_dim_ok(H, 16384) && ek_ok(E, K) && pf_dim_ok(I, 4096) &&
+           (Is == 0 || pf_dim_ok(Is, 4096)) &&
+           (uint64_t)T * K * I * 2 + (uint64_t)I * 2 < (1ull << 32);
+}
+
 } // namespace
+
+static moe_status layer_prefill(const void *x, const void *w_router, const void *w13,
+                                const void *w2, const void *w_gate_up, const void *w_down, int T,
+                                int H, int E, int I, int K, int Is, int renormalize,
+                                int32_t *topk_ids, float *topk_w, float *logits, void *y,
+                                void *ws, size_t ws_bytes, int stage, hipStream_t stream)
+{
+    const bool shared = w_gate_up != nullptr || w_down != nullptr;
+    if (!shared) Is = 0;
+    if (!pf_shape_ok(T, H, E, I, K, Is) || (shared && Is == 0)) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!x || !w_router || !w13 || !w2 || !topk_ids || !topk_w || !logits || !y || !ws ||
+        (shared && (!w_gate_up || !w_down)))
+        return MOE_ERR_NULL;
+    if (!al(x, 16) || !al(w_router, 16) || !al(w13, 16) || !al(w2, 16) || !al(topk_ids, 4) ||
+        !al(topk_w, 4) || !al(logits, 4) || !al(y, 2) || !al(ws, 256) ||
+        (shared && (!al(w_gate_up, 16) || !al(w_down, 16))))
+        return MOE_ERR_ALIGN;
+    if (ws_bytes < prefill_layout(T, H, E, I, K, Is).bytes) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_prefill(x, w_router, w13, w2, w_gate_up, w_down, T, H, E, I, K, Is,
+                                     renormalize, topk_ids, topk_w, logits, y, ws, stage, stream));
+}
 
 // moe_layer_decode; stage > 0 (three-launch path only) runs that launch alone.
 static moe_status layer_decode(const void *x, const void *w_router, const void *w13,
@@ -167,6 +201,33 @@ int moe_layer_launches(int M, int H, int E, int I, int K, int Is)
     if (lean_m_ok(M, H, E, I, K, Is)) return 4;
     // shared_expert (2) + moe_route (2) + moe_decode_fused (2)
     return (Is ? 2 : 0) + 2 + 2;
+}
+
+size_t moe_prefill_workspace_bytes(int T, int H, int E, int I, int K, int Is)
+{
+    if (!pf_shape_ok(T, H, E, I, K, Is)) return 0;
+    return prefill_layout(T < 1 ? 1 : T, H, E, I, K, Is).bytes;
+}
+
+moe_status moe_layer_prefill(const void *x, const void *w_router, const void *w13,
+                             const void *w2, const void *w_gate_up, const void *w_down, int T,
+                             int H, int E, int I, int K, int Is, int renormalize,
+                             int32_t *topk_ids, float *topk_w, float *logits, void *y, void *ws,
+                             size_t ws_bytes, hipStream_t stream)
+{
+    return layer_prefill(x, w_router, w13, w2, w_gate_up, w_down, T, H, E, I, K, Is, renormalize,
+                         topk_ids, topk_w, logits, y, ws, ws_bytes, 0, stream);
+}
+
+moe_status moe_dbg_prefill_stage(int stage, const void *x, const void *w_router, const void *w13,
+                                 const void *w2, const void *w_gate_up, const void *w_down,
+                                 int T, int H, int E, int I, int K, int Is, int renormalize,
+                                 int32_t *topk_ids, float *topk_w, float *logits, void *y,
+                                 void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (stage < 1 || stage > 6) return MOE_ERR_SHAPE;
+    return layer_prefill(x, w_router, w13, w2, w_gate_up, w_down, T, H, E, I, K, Is, renormalize,
+                         topk_ids, topk_w, logits, y, ws, ws_bytes, stage, stream);
 }
 
 moe_status moe_probe_empty(hipStream_t stream) { return hip_status(launch_probe_empty(stream)); }

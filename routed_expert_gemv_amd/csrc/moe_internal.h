@@ -37,6 +37,31 @@ constexpr size_t kSharedOutOffset = kGroupOffset + align256(sizeof(GroupTable));
 constexpr size_t kSharedOutBytes = (size_t)kMaxTokens * 4096 * sizeof(float);
 constexpr size_t kRoutedActOffset = kSharedOutOffset + align256(kSharedOutBytes);
 
+// Many-token (prefill) layer: per-call plan in the workspace.
+constexpr int kPrefillRows = 128; // token rows per grouped-GEMM tile
+struct PrefillPlan {
+    int total13; // W13 tiles (routed + shared)
+    int total2;  // W2 tiles
+    int pairs;   // (token, slot) pairs with a valid expert id
+    int pad_[61];
+    int count[kMaxExperts]; // pairs per expert
+    int start[kMaxExperts]; // first entry of each expert in the pair list
+};
+// Byte offsets of the prefill workspace regions (256-byte aligned) and the
+// W13 / W2 grid sizes (multiples of 8, at least the largest tile count).
+struct PrefillLayout {
+    size_t plan, desc13, desc2, perm, act, act_s, down, bytes;
+    int grid13, grid2;
+};
+PrefillLayout prefill_layout(int T, int H, int E, int I, int K, int Is);
+// stage 0: all launches; 1..6: router, top-k, plan, W13, W2, down + combine alone.
+hipError_t launch_prefill(const void *x, const void *wr, const void *w13, const void *w2,
+                          const void *wsgu, const void *wsd, int T, int H, int E, int I, int K,
+                          int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
+                          void *ws, int stage, hipStream_t s);
+hipError_t launch_topk(const float *logits, int M, int E, int K, int renorm, int32_t *ids,
+                       float *w, hipStream_t s);
+
 inline int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 
 hipError_t launch_route(const void *x, const void *wr, int M, int H, int E, int K, int renorm,

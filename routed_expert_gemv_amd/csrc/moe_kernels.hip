@@ -1142,6 +1142,12 @@ hipError_t launch_route(const void *x, const void *wr, int M, int H, int E, int 
     default: return hipErrorInvalidValue;
     }
     if (err != hipSuccess) return err;
+    return launch_topk(logits, M, E, K, renorm, ids, w, s);
+}
+
+hipError_t launch_topk(const float *logits, int M, int E, int K, int renorm, int32_t *ids,
+                       float *w, hipStream_t s)
+{
     if (E <= kWave)
         hipLaunchKernelGGL(k_topk<1>, dim3(M), dim3(kWave), 0, s, logits, E, K, renorm, ids, w);
     else if (E <= 4 * kWave)

@@ -1,6 +1,7 @@
 """The C-ABI library without a GPU: it loads, exports every function that
-include/moe_decode.h declares, and rejects bad arguments on the host before
-anything is enqueued (no call here reaches a kernel launch)."""
+include/moe_decode.h and include/moe_prefill.h declare, and rejects bad
+arguments on the host before anything is enqueued (no call here reaches a
+kernel launch)."""
 import ctypes as C
 import os
 import re
@@ -13,29 +14,34 @@ from routed_expert_gemv_amd import _lib, build, synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+HEADERS = [HEADER, os.path.join(ROOT, "include", "moe_prefill.h")]
 
 FAKE = 0x10000       # aligned, never dereferenced: validation fails first
 FAKE_ODD = 0x10002   # 2-byte aligned only
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^(?:moe_status|int|size_t|const char \*)\s*(\w+)\s*\(", text, flags=re.M)
+    names = []
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names += re.findall(r"^(?:moe_status|int|size_t|const char \*)\s*(\w+)\s*\(", text,
+                            flags=re.M)
+    return names
 
 
 def test_library_builds_and_loads():
     assert os.path.exists(build.LIB) or build.build(force=True)
     L = _lib.lib()
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert set(names) >= {"moe_route", "shared_expert", "moe_decode_fused", "moe_workspace_bytes"}
+    assert set(names) >= {"moe_route", "shared_expert", "moe_decode_fused", "moe_workspace_bytes",
+                          "moe_layer_prefill", "moe_prefill_workspace_bytes"}
     L = C.CDLL(build.LIB)
     for n in names:
-        assert hasattr(L, n), "symbol %s declared in moe_decode.h is not exported" % n
+        assert hasattr(L, n), "declared symbol %s is not exported" % n
     assert set(names) == set(_lib.EXPORTED)
 
 
@@ -192,3 +198,55 @@ def test_layer_stage_probe_validation():
     assert call(2, H=2000) == -2
     assert L.moe_dbg_layer_stage(2, None, FAKE, FAKE, FAKE, None, None, 1, 2048, 256, 512, 8, 0, 1,
                                  FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+
+
+def test_prefill_workspace_bytes():
+    L = _lib.lib()
+    T, H, E, I, K, Is = 2048, 2048, 256, 512, 8, 512
+    n = L.moe_prefill_workspace_bytes(T, H, E, I, K, Is)
+    # at least the down products [T*K, H] fp32 and both activations (fp16)
+    assert n >= T * K * H * 4 + T * K * I * 2 + T * Is * 2 and n % 256 == 0
+    assert L.moe_prefill_workspace_bytes(T, H, E, I, K, 0) < n
+    assert L.moe_prefill_workspace_bytes(T + 1, H, E, I, K, Is) > n
+    assert L.moe_prefill_workspace_bytes(0, H, E, I, K, Is) > 0          # T = 0: valid
+    assert L.moe_prefill_workspace_bytes(65537, H, E, I, K, Is) == 0     # T too large
+    assert L.moe_prefill_workspace_bytes(T, 2000, E, I, K, Is) == 0      # H % 64
+    assert L.moe_prefill_workspace_bytes(T, H, E, 96, K, Is) == 0        # I % 64
+    assert L.moe_prefill_workspace_bytes(T, H, E, I, K, 32) == 0         # Is % 64
+    assert L.moe_prefill_workspace_bytes(T, H, 1025, I, K, Is) == 0      # E
+    assert L.moe_prefill_workspace_bytes(T, H, 4, I, 8, Is) == 0         # K > E
+    assert L.moe_prefill_workspace_bytes(T, 64, 16, 64, 4, 64) > 0       # smallest dims
+
+
+def test_prefill_validation():
+    L = _lib.lib()
+    shape = dict(T=256, H=2048, E=256, I=512, K=8, Is=512)
+    need = L.moe_prefill_workspace_bytes(*shape.values())
+
+    def call(fn=L.moe_layer_prefill, pre=(), x=FAKE, wr=FAKE, w13=FAKE, w2=FAKE, gu=FAKE, d=FAKE,
+             ids=FAKE, tw=FAKE, lg=FAKE, y=FAKE, ws=FAKE, n=need, **kw):
+        a = dict(shape, **kw)
+        return fn(*pre, x, wr, w13, w2, gu, d, a["T"], a["H"], a["E"], a["I"], a["K"], a["Is"], 1,
+                  ids, tw, lg, y, ws, n, None)
+
+    assert call(x=None) == -1
+    assert call(y=None) == -1
+    assert call(gu=None) == -1            # one of the shared pair missing
+    assert call(T=-1) == -2
+    assert call(T=65537) == -2
+    assert call(H=2000) == -2
+    assert call(I=96) == -2
+    assert call(K=0) == -2
+    assert call(E=1025) == -2
+    assert call(Is=0) == -2               # shared weights given but Is = 0
+    assert call(w13=FAKE_ODD) == -3
+    assert call(ws=FAKE + 16) == -3
+    assert call(n=need - 1) == -4
+    assert call(T=0) == 0                 # empty call: nothing enqueued
+    # without a shared expert Is is ignored and the workspace is smaller
+    small = L.moe_prefill_workspace_bytes(256, 2048, 256, 512, 8, 0)
+    assert call(gu=None, d=None, Is=0, n=small - 1) == -4
+    # the stage probe: stage 1..6 only, same validation
+    assert call(fn=L.moe_dbg_prefill_stage, pre=(0,)) == -2
+    assert call(fn=L.moe_dbg_prefill_stage, pre=(7,)) == -2
+    assert call(fn=L.moe_dbg_prefill_stage, pre=(4,), x=None) == -1
