@@ -18,6 +18,12 @@ fraction of the 8 TB/s HBM peak, the roofline of the dominant kernel (the
 expand kernel; every kernel of every layer timed with HIP events that the
 library records on the stream the kernels run on) and the fp64 oracle timed on
 this host's cores on a bounded sample of the same layers.
+
+With --prefill T the workload is the many-token layer instead: a stack of
+full-width layers (default 8) with T tokens each, every layer one
+moe_layer_prefill call (seven launches); the line reports tokens/s through a
+layer, us/layer, weight bytes per second, and the roofline of the gate/up
+grouped GEMM.
 """
 from __future__ import annotations
 
@@ -37,6 +43,14 @@ LAYERS = 36
 COUNTERS = os.path.join(ROOT, "profiles", "k_expand_counters_full_e256_k8_i512.json")
 STAGES = ("k_router_shared", "k_expand", "k_reduce")
 KERNEL_SRC = os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", "moe_kernels.hip")
+PF_METRIC = "MoE prefill tokens/s through one full-width layer (T tokens per layer)"
+PF_STAGES = ("k_pf_router", "k_pf_topk", "k_pf_plan", "k_pf_w13", "k_pf_w2", "k_pf_combine")
+PF_KERNEL_SRC = os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", "moe_prefill.hip")
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def pf_counters_path(T):
+    return os.path.join(ROOT, "profiles", "k_pf_w13_counters_prefill_t%d_e256_k8_i512.json" % T)
 
 
 def log(*a):
@@ -63,14 +77,37 @@ def stage_bytes(sh):
     return dict(zip(STAGES, (router, expand, reduce)))
 
 
-def counters_traffic():
-    """HBM traffic per launch of the expand kernel from the committed rocprofv3
+def prefill_stage_bytes(sh, n_distinct):
+    """Algorithmic bytes of each prefill launch (T = sh.M tokens, n_distinct
+    experts with at least one token): weights read once, x read once, and the
+    tensors each kernel writes or reads (logits, ids/weights, pair lists,
+    activations, the fp32 down products, y)."""
+    T, H, E, K, I, Is = sh.M, sh.H, sh.E, sh.K, sh.I, sh.Is
+    rows = T * K + (T if Is else 0)
+    return dict(zip(PF_STAGES, (
+        2 * E * H + 2 * T * H + 4 * T * E,
+        4 * T * E + 8 * T * K,
+        4 * T * K * 2,
+        n_distinct * 2 * 2 * I * H + 2 * 2 * Is * H + 2 * T * H + 2 * T * K * I + 2 * T * Is,
+        n_distinct * 2 * H * I + 2 * H * Is + 2 * T * K * I + 2 * T * Is + 4 * rows * H,
+        4 * rows * H + 4 * T * K + 2 * T * H)))
+
+
+def prefill_flops(sh):
+    """Multiply-add flops of the router, gate/up and down products (x2 per MAC)."""
+    T, H, E, K, I, Is = sh.M, sh.H, sh.E, sh.K, sh.I, sh.Is
+    return {"k_pf_router": 2 * T * E * H, "k_pf_w13": 2 * T * (K * 2 * I + 2 * Is) * H,
+            "k_pf_w2": 2 * T * (K * I + Is) * H}
+
+
+def counters_traffic(path=COUNTERS, src=KERNEL_SRC):
+    """HBM traffic per launch of the summarised kernel from a committed rocprofv3
     counter summary, if it was taken on the current kernel source; else None."""
     try:
-        c = json.load(open(COUNTERS))
+        c = json.load(open(path))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if c.get("kernel_source_sha256") != sha:
         return None
     return c.get("hbm_bytes_per_dispatch")
@@ -151,6 +188,138 @@ def time_stages(layers, reps):
     return us, reps * len(layers)
 
 
+def prefill_cpu_baseline(t, sh, budget_s=12.0):
+    """The fp64 oracle, as it is, on this host's cores: router, top-K, the K
+    experts and the shared expert of sampled tokens of one prefill layer.  The
+    layer's tensors are widened to fp64 on the host once, before timing; only
+    the oracle's own calls are timed (the gather of each token's expert slices
+    between them is not)."""
+    import numpy as np
+    import torch
+    import oracle
+
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    h = {k: t[k].detach().to("cpu", torch.float64).numpy()
+         for k in ("x", "wr", "wsgu", "wsd", "w13", "w2")}
+    order = np.random.default_rng(0).permutation(sh.M)
+    done, el = 0, 0.0
+    while el < budget_s and done < sh.M:
+        m = int(order[done])
+        t0 = time.perf_counter()
+        lg = oracle.router_logits(h["x"][m], h["wr"], nthreads)
+        ids, w, _ = oracle.topk_softmax(lg, sh.K, sh.renormalize)
+        el += time.perf_counter() - t0
+        w13sel, w2sel = h["w13"][ids], h["w2"][ids]
+        t0 = time.perf_counter()
+        oracle.token_output(h["x"][m], w13sel, w2sel, w, h["wsgu"], h["wsd"], nthreads)
+        el += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": nthreads,
+            "kind": "oracle", "us_per_token": round(el / done * 1e6, 1),
+            "sample": "%d tokens of layer 0 (fp64 C oracle per token: router, top-k, 8 experts, "
+                      "shared expert), %.1f s of oracle time" % (done, el)}
+
+
+def time_prefill_stages(layers, reps):
+    """Average duration of each of the six prefill stages: per stage, a
+    hipGraph of that launch alone for every layer (inputs left by full calls),
+    replayed `reps` times between two HIP events on the replay stream."""
+    import torch
+
+    for layer in layers:
+        layer.forward()
+    torch.cuda.synchronize()
+    us = {}
+    for i, name in enumerate(PF_STAGES):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for layer in layers:
+                layer.stage(i + 1)
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us[name] = a.elapsed_time(b) * 1e3 / (reps * len(layers))
+        del g
+    return us, reps * len(layers)
+
+
+def prefill_main(args, dev):
+    import torch
+    from routed_expert_gemv_amd import synth
+    from routed_expert_gemv_amd.api import prefill_workspace
+    from routed_expert_gemv_amd.stack import DecodeStack, PrefillLayer
+
+    T = args.prefill
+    n_layers = args.layers if args.layers_given else 8
+    sh = synth.LayerShape(M=T, H=2048, E=256, K=8, I=512, Is=512)
+    log("drawing %d prefill layers of %d tokens (seeds 0..%d) on %s" % (n_layers, T, n_layers - 1, dev))
+    tensors = [synth.draw_layer(sh, s, dev) for s in range(n_layers)]
+    ws = prefill_workspace(T, sh.H, sh.E, sh.I, sh.K, sh.Is, dev)
+    layers = [PrefillLayer(t, sh, ws) for t in tensors]
+    stack = DecodeStack(layers)
+    stack.capture()
+    for _ in range(args.warmup):
+        stack.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        stack.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms_step = a.elapsed_time(b) / args.steps
+    us_layer = ms_step * 1e3 / n_layers
+    n_distinct = [len(set(l.topk_ids.flatten().tolist())) for l in layers]
+    nd = sum(n_distinct) / len(n_distinct)
+    w_bytes = nd * 3 * 2 * sh.I * sh.H + 3 * 2 * sh.Is * sh.H + 2 * sh.E * sh.H
+    log("%.3f ms/replay, %.1f us/layer, %.0f tokens/s, %.0f GB/s of weights"
+        % (ms_step, us_layer, T / (us_layer * 1e-6), w_bytes / (us_layer * 1e-6) / 1e9))
+    st_us, n_launch = time_prefill_stages(layers, args.launch_reps)
+    st_b = prefill_stage_bytes(sh, round(nd))
+    fl = prefill_flops(sh)
+    log("kernels: " + ", ".join("%s %.1f us %.0f GB/s" % (k, st_us[k], st_b[k] / (st_us[k] * 1e-6) / 1e9)
+                                 for k in PF_STAGES))
+    dom = "k_pf_w13"
+    k_gbs = st_b[dom] / (st_us[dom] * 1e-6) / 1e9
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+            "traffic": counters_traffic(pf_counters_path(T), PF_KERNEL_SRC),
+            "avg_launch_us": round(st_us[dom], 3), "bytes_per_launch": st_b[dom],
+            "launches_timed": n_launch,
+            "mfma_tflops": round(fl[dom] / (st_us[dom] * 1e-6) / 1e12, 1),
+            "mfma_frac": round(fl[dom] / (st_us[dom] * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "per_kernel_us": {k: round(v, 3) for k, v in st_us.items()},
+            "per_kernel_bytes": st_b}
+    out = {
+        "metric": PF_METRIC, "value": round(T / (us_layer * 1e-6), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "%d-layer full-width MoE prefill stack as one hipGraph: T=%d "
+                               "tokens per layer, H=2048, E=256, top-8 renormalised, I=512, "
+                               "shared Is=512, fp16" % (n_layers, T),
+                   "tokens": T, "layers": n_layers, "layer_seeds": "0..%d" % (n_layers - 1),
+                   "distinct_experts_per_layer": round(nd, 2)},
+        "us_per_layer": round(us_layer, 3),
+        "weight_gbs": round(w_bytes / (us_layer * 1e-6) / 1e9, 1),
+        "frac_of_peak": round(w_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host (~%.0f s)" % args.cpu_budget)
+        out["cpu_baseline"] = prefill_cpu_baseline(tensors[0], sh, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
 # ---------------------------------------------------------------- rocprofv3 helpers
 COPY_BYTES = 1 << 30
 
@@ -172,9 +341,14 @@ def counters_pass(args):
         moe.moe_probe_copy(src, dst)
     torch.cuda.synchronize()
     del src, dst
-    sh = synth.SHAPES["full_e256_k8_i512" if args.tokens == 1 else
-                      "batch%d_e256_k8_i512" % args.tokens]
-    layers = [DecodeLayer(synth.draw_layer(sh, s, dev), sh) for s in range(args.layers)]
+    if args.prefill:
+        from routed_expert_gemv_amd.stack import PrefillLayer
+        sh = synth.LayerShape(M=args.prefill, H=2048, E=256, K=8, I=512, Is=512)
+        layers = [PrefillLayer(synth.draw_layer(sh, s, dev), sh) for s in range(args.layers)]
+    else:
+        sh = synth.SHAPES["full_e256_k8_i512" if args.tokens == 1 else
+                          "batch%d_e256_k8_i512" % args.tokens]
+        layers = [DecodeLayer(synth.draw_layer(sh, s, dev), sh) for s in range(args.layers)]
     for _ in range(2):
         for l in layers:
             l.forward()
@@ -192,7 +366,7 @@ def _read_csv_rows(d, suffix):
     return rows
 
 
-def summarize_counters(fetch_dir, write_dir, out_path, cmds):
+def summarize_counters(fetch_dir, write_dir, out_path, cmds, prefill=0):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE of the expand kernel (and, for
     context, the other two), scaled by what the same counters read for the
     1 GiB copy, into a JSON summary."""
@@ -210,8 +384,9 @@ def summarize_counters(fetch_dir, write_dir, out_path, cmds):
                 copy.append(v)
         return mine, copy
 
-    fw, fc = per_kernel(fetch_dir, "FETCH_SIZE")
-    ww, wc = per_kernel(write_dir, "WRITE_SIZE")
+    kern = "k_pf_w13" if prefill else "k_expand"
+    fw, fc = per_kernel(fetch_dir, "FETCH_SIZE", kern)
+    ww, wc = per_kernel(write_dir, "WRITE_SIZE", kern)
     if not fw or not fc or not ww or not wc:
         raise SystemExit("counter rows missing: fetch %d/%d write %d/%d" % (len(fw), len(fc), len(ww), len(wc)))
     kib = 1024.0
@@ -220,28 +395,40 @@ def summarize_counters(fetch_dir, write_dir, out_path, cmds):
     fetch_b = (sum(fw) / len(fw)) * kib / fetch_scale
     write_b = (sum(ww) / len(ww)) * kib / write_scale
     from routed_expert_gemv_amd import synth
-    sh = synth.SHAPES["full_e256_k8_i512"]
+    if prefill:
+        sh = synth.LayerShape(M=prefill, H=2048, E=256, K=8, I=512, Is=512)
+        algo = prefill_stage_bytes(sh, sh.E)  # every expert receives tokens at this size
+        other_names = ("k_pf_router", "k_pf_w2", "k_pf_combine")
+    else:
+        sh = synth.SHAPES["full_e256_k8_i512"]
+        algo = stage_bytes(sh)
+        other_names = ("k_router_shared", "k_reduce")
     others = {}
-    for k in ("k_router_shared", "k_reduce"):
+    for k in other_names:
         f, _ = per_kernel(fetch_dir, "FETCH_SIZE", k)
         w, _ = per_kernel(write_dir, "WRITE_SIZE", k)
         if f and w:
             others[k] = {"hbm_bytes_per_dispatch": int(round((sum(f) / len(f)) * kib / fetch_scale
                                                              + (sum(w) / len(w)) * kib / write_scale)),
-                         "algorithmic_bytes_per_dispatch": stage_bytes(sh)[k]}
+                         "algorithmic_bytes_per_dispatch": algo[k]}
     res = {
-        "kernel": "k_expand<4,4,64,1> (routed gate/up + SiLU*mul, shared down), M=1",
-        "workload": "full-width layer H=2048 E=256 K=8 I=512 Is=512, M=1, 36 layers rotating",
+        "kernel": ("k_pf_w13 (grouped gate/up GEMM + SiLU*mul, routed and shared experts), T=%d"
+                   % prefill) if prefill else
+                  "k_expand<4,4,64,1> (routed gate/up + SiLU*mul, shared down), M=1",
+        "workload": ("full-width prefill layer H=2048 E=256 K=8 I=512 Is=512, T=%d tokens"
+                     % prefill) if prefill else
+                    "full-width layer H=2048 E=256 K=8 I=512 Is=512, M=1, 36 layers rotating",
         "commands": cmds,
         "fetch_size_kib_per_dispatch": sum(fw) / len(fw),
         "write_size_kib_per_dispatch": sum(ww) / len(ww),
         "copy_fetch_kib": sum(fc) / len(fc), "copy_write_kib": sum(wc) / len(wc),
         "copy_bytes": COPY_BYTES, "fetch_scale": fetch_scale, "write_scale": write_scale,
         "hbm_bytes_per_dispatch": int(round(fetch_b + write_b)),
-        "algorithmic_bytes_per_dispatch": stage_bytes(sh)["k_expand"],
+        "algorithmic_bytes_per_dispatch": algo[kern],
         "dispatches": len(fw),
         "other_kernels": others,
-        "kernel_source_sha256": hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest(),
+        "kernel_source_sha256": hashlib.sha256(open(PF_KERNEL_SRC if prefill else KERNEL_SRC,
+                                                    "rb").read()).hexdigest(),
     }
     with open(out_path, "w") as fh:
         json.dump(res, fh, indent=1)
@@ -336,7 +523,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers in the stack (decode default %d, prefill default 8)" % LAYERS)
+    ap.add_argument("--prefill", type=int, default=0, metavar="T",
+                    help="bench the many-token layer with T tokens per layer instead of decode")
     ap.add_argument("--tokens", type=int, default=1, choices=(1, 2, 4, 8),
                     help="tokens per layer: 1 (the default workload) or a small decode batch "
                          "(each token routed on its own; distinct experts read once)")
@@ -354,9 +544,12 @@ def main():
     ap.add_argument("--cmd", action="append", default=[],
                     help="command line(s) recorded in a summary")
     args = ap.parse_args()
+    args.layers_given = args.layers is not None
+    if args.layers is None:
+        args.layers = LAYERS
 
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, cmds=args.cmd)
+        summarize_counters(*args.summarize_counters, cmds=args.cmd, prefill=args.prefill)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, cmd=" && ".join(args.cmd))
@@ -378,6 +571,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.counters_pass:
         counters_pass(args)
+        return
+    if args.prefill:
+        prefill_main(args, dev)
         return
     sh = synth.SHAPES["full_e256_k8_i512" if args.tokens == 1 else
                       "batch%d_e256_k8_i512" % args.tokens]

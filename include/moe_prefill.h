@@ -49,9 +49,13 @@ size_t moe_prefill_workspace_bytes(int T, int H, int E, int I, int K, int Is);
  *              k in routing order in fp32, one rounding
  *   ws         >= moe_prefill_workspace_bytes(...) bytes; scratch only.  Calls
  *              sharing a ws must not overlap in time.
- * Six launches: router GEMM, top-K, the plan (one workgroup), gate/up GEMM
- * with SiLU*mul (routed experts and the shared expert), down GEMM, shared
- * down GEMM with the combine (the combine alone without a shared expert).
+ * Seven launches: the router GEMM (in slices of H) and the ordered sum of its
+ * slices, top-K, the plan (one workgroup: per-expert pair lists and tile
+ * lists), the gate/up grouped GEMM with SiLU*mul (routed experts plus the
+ * shared expert as one more group), the down grouped GEMM (same groups; fp32
+ * products per (token, slot) and per token for the shared expert), and the
+ * combine: weighted sum in routing order plus the shared output, one fp16
+ * rounding.
  * The routed activations are rounded to fp16 before the down products. */
 moe_status moe_layer_prefill(const void *x, const void *w_router, const void *w13,
                              const void *w2, const void *w_gate_up, const void *w_down, int T,
@@ -59,10 +63,10 @@ moe_status moe_layer_prefill(const void *x, const void *w_router, const void *w1
                              int32_t *topk_ids, float *topk_w, float *logits, void *y, void *ws,
                              size_t ws_bytes, hipStream_t stream);
 
-/* Test-only: one of moe_layer_prefill's six launches alone (stage 1..6 in the
- * order above), for timing each kernel.  A stage reads what the previous ones
- * left in the same buffers; arguments as for moe_layer_prefill; MOE_ERR_SHAPE
- * for a stage outside 1..6. */
+/* Test-only: one stage of moe_layer_prefill alone, for timing each kernel:
+ * 1 router (both launches), 2 top-K, 3 plan, 4 gate/up, 5 down, 6 combine.
+ * A stage reads what the previous ones left in the same buffers; arguments as
+ * for moe_layer_prefill; MOE_ERR_SHAPE for a stage outside 1..6. */
 moe_status moe_dbg_prefill_stage(int stage, const void *x, const void *w_router, const void *w13,
                                  const void *w2, const void *w_gate_up, const void *w_down,
                                  int T, int H, int E, int I, int K, int Is, int renormalize,

@@ -332,7 +332,7 @@ def moe_layer_prefill(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int 
 def moe_dbg_prefill_stage(stage: int, x, w_router, w13, w2, w_gate_up=None, w_down=None,
                           K: int = 8, renormalize: bool = True, topk_ids=None, topk_w=None,
                           logits=None, y=None, ws=None, stream=None):
-    """One of moe_layer_prefill's six launches alone (test-only; for timing)."""
+    """One of moe_layer_prefill's six stages alone (test-only; for timing)."""
     out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
                             topk_w, logits, y, ws, prefill_workspace)
     _check("moe_dbg_prefill_stage",

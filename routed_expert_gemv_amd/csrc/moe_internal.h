@@ -50,11 +50,12 @@ struct PrefillPlan {
 // Byte offsets of the prefill workspace regions (256-byte aligned) and the
 // W13 / W2 grid sizes (multiples of 8, at least the largest tile count).
 struct PrefillLayout {
-    size_t plan, desc13, desc2, perm, act, act_s, down, bytes;
-    int grid13, grid2;
+    size_t plan, part, desc13, desc2, perm, act, act_s, down, bytes;
+    int grid13, grid2, router_split;
 };
 PrefillLayout prefill_layout(int T, int H, int E, int I, int K, int Is);
-// stage 0: all launches; 1..6: router, top-k, plan, W13, W2, down + combine alone.
+// stage 0: all launches; 1..6: router (partial GEMMs + their sum), top-k, plan,
+// W13, W2, combine alone.
 hipError_t launch_prefill(const void *x, const void *wr, const void *w13, const void *w2,
                           const void *wsgu, const void *wsd, int T, int H, int E, int I, int K,
                           int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,

@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -42,10 +44,12 @@ constexpr int kBM = kPrefillRows;       // token rows per grouped-GEMM tile: eig
 constexpr int kBK = 64;                 // k per main-loop step (two 32-wide MFMA steps)
 constexpr int kLdsRow = kBK + 8;        // halves per staged row (144 bytes)
 constexpr int kRouterRows = 64;         // token rows per router tile
-constexpr int kGemmWaves = 8;           // waves per grouped-GEMM workgroup
+constexpr int kGemmWaves = 4;           // waves per grouped-GEMM workgroup
+constexpr int kDepth = 2;               // k steps in flight in the GEMM main loops
 // Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanIds = 16;            // expert ids per plan thread per pass
 
 __device__ __forceinline__ f16x8 ld16(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 
@@ -93,26 +97,37 @@ __device__ __forceinline__ TokRows<SL> tok_rows(const f16 *src, uint32_t src_byt
     return a;
 }
 
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, class F>
+__device__ __forceinline__ void unroll(F &&f)
+{
+    if constexpr (N > 0) {
+        unroll<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
 // acc[mt][ct] += A(rows 16 mt .. 16 mt + 15) * B(ct)^T over kdim for one wave
 // (MT row tiles of 16 tokens, NCT column tiles of 16 weight rows), in a
-// workgroup of WAVES waves.
+// workgroup of WAVES waves, with D k steps in flight.
 //   a.off[i]: byte offset of this thread's token row for staging chunk i
 //             (tile row t/8 + 8 WAVES i), whose 16-byte chunk t % 8 of each k
 //             step it copies into LDS;
 //   brow[ct]: this lane's weight row (row lane % 16 of column tile ct); a
 //             wave without valid columns passes clamped valid rows, computes
 //             products anyway and does not store them;
-//   b0: the first k step of the weight rows, already loaded by the caller.
+//   bb[0]:    the first k step of the weight rows, already loaded by the
+//             caller; bb[1..D] are this function's other weight buffers.
 // Every thread of the block must call this (it contains barriers).  The
-// token tile is double-buffered in LDS and, like the weights, loaded into
-// registers two k steps ahead (two steps in flight while one is multiplied).
+// token tile is double-buffered in LDS; token rows and weights are loaded
+// into registers D steps ahead of their products.
 template <int WAVES, int MT>
 constexpr int stage_loads() { return MT * 16 * kBK / 8 / (64 * WAVES); } // 16-byte loads per thread
 
-template <int WAVES, int MT, int NCT>
+template <int WAVES, int MT, int NCT, int D>
 __device__ __forceinline__ void mfma_rows(const TokRows<stage_loads<WAVES, MT>()> &arows,
                                           const f16 *const (&brow)[NCT], int kdim, f16 *lds,
-                                          f16x8 (&b0)[NCT][2], f32x4 (&acc)[MT][NCT])
+                                          f16x8 (&bb)[D + 1][NCT][2], f32x4 (&acc)[MT][NCT])
 {
     constexpr int kStageLoads = stage_loads<WAVES, MT>();
     static_assert(kStageLoads >= 1, "tile too small for the workgroup");
@@ -126,18 +141,16 @@ __device__ __forceinline__ void mfma_rows(const TokRows<stage_loads<WAVES, MT>()
 #pragma unroll
     for (int i = 0; i < kStageLoads; ++i) wofs[i] = (t / 8 + 8 * WAVES * i) * kLdsRow + kc * 8;
     const int rofs = (lane & 15) * kLdsRow + 8 * quarter;
-    typedef f16x8 TokRegs[kStageLoads];
-    TokRegs a0, a1, a2;
-    f16x8 b1[NCT][2], b2[NCT][2];
+    f16x8 aa[D + 1][kStageLoads];
 
-    auto load_a = [&](int k, TokRegs &a) {
+    auto load_a = [&](int k, f16x8 (&a)[kStageLoads]) {
 #pragma unroll
         for (int i = 0; i < kStageLoads; ++i)
             a[i] = __builtin_bit_cast(
                 f16x8, __builtin_amdgcn_raw_buffer_load_b128(
                            arows.rsrc, arows.off[i] + (uint32_t)(k * kBK + kc * 8) * 2, 0, 0));
     };
-    auto store_a = [&](const TokRegs &a, int st) {
+    auto store_a = [&](const f16x8 (&a)[kStageLoads], int st) {
 #pragma unroll
         for (int i = 0; i < kStageLoads; ++i)
             *reinterpret_cast<f16x8 *>(lds + st * kLdsStage + wofs[i]) = a[i];
@@ -155,42 +168,45 @@ __device__ __forceinline__ void mfma_rows(const TokRows<stage_loads<WAVES, MT>()
                         __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[ct][s], acc[mt][ct], 0, 0, 0);
             }
     };
-    // One k step: products of step k (LDS stage k & 1, weights bc) while the
-    // token rows and weights of step k + 2 load (into an, bn); the token rows
-    // of step k + 1, loaded one step earlier (ast), go to the other LDS stage.
-    // Load indices are clamped to the last step, so no load sits under a
-    // branch: the compiler then waits for exactly the loads each use needs
-    // (the clamped repeats near the end re-read rows just read, from L2).
-    auto step = [&](int k, const f16x8 (&bc)[NCT][2], f16x8 (&bn)[NCT][2], const TokRegs &ast,
-                    TokRegs &an) {
-        load_a(min(k + 2, nk - 1), an);
-        load_b<NCT>(brow, min(k + 2, nk - 1), quarter, bn);
-        mma(k & 1, bc);
-        store_a(ast, (k + 1) & 1);
-        __syncthreads();
-    };
 
-    load_b<NCT>(brow, min(1, nk - 1), quarter, b1);
-    load_a(0, a0);
-    load_a(min(1, nk - 1), a1);
-    store_a(a0, 0);
+    // prologue: steps 0 .. D-1 in flight, step 0's token rows into LDS stage 0
+    unroll<D>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if constexpr (j > 0) load_b<NCT>(brow, min(j, nk - 1), quarter, bb[j]);
+        load_a(min(j, nk - 1), aa[j]);
+    });
+    store_a(aa[0], 0);
     __syncthreads();
-    // top of each pass: weights of steps k, k + 1 in b0, b1; token rows of
-    // step k in LDS stage k & 1, of step k + 1 in a1
+    // Step k: products from LDS stage k & 1 and bb[k % (D+1)] while step
+    // k + D loads into the buffers step k - 1 freed; step k + 1's token rows
+    // go to the other LDS stage.  Load indices are clamped to the last step,
+    // so no load sits under a branch: the compiler then waits for exactly the
+    // loads each use needs (the clamped repeats near the end re-read rows just
+    // read, from L2).
     int k = 0;
-    for (; k + 3 <= nk; k += 3) {
-        step(k, b0, b2, a1, a2);
-        step(k + 1, b1, b0, a2, a0);
-        step(k + 2, b2, b1, a0, a1);
+    for (; k + D + 1 <= nk; k += D + 1) {
+        unroll<D + 1>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const int kk = k + j;
+            load_a(min(kk + D, nk - 1), aa[(j + D) % (D + 1)]);
+            load_b<NCT>(brow, min(kk + D, nk - 1), quarter, bb[(j + D) % (D + 1)]);
+            mma(kk & 1, bb[j]);
+            store_a(aa[(j + 1) % (D + 1)], (kk + 1) & 1);
+            __syncthreads();
+        });
     }
-    if (k + 1 == nk) {
-        mma(k & 1, b0);
-    } else if (k + 2 == nk) {
-        mma(k & 1, b0);
-        store_a(a1, (k + 1) & 1);
-        __syncthreads();
-        mma((k + 1) & 1, b1);
-    }
+    // the last nk - k (< D + 1) steps: everything is loaded already
+    const int r = nk - k;
+    unroll<D + 1>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if (j < r) {
+            mma((k + j) & 1, bb[j]);
+            if (j + 1 < r) {
+                store_a(aa[(j + 1) % (D + 1)], (k + j + 1) & 1);
+                __syncthreads();
+            }
+        }
+    });
 }
 
 // Tile descriptor written by the plan: x = group | n_tile << 11 | rows << 22
@@ -212,35 +228,43 @@ __device__ __forceinline__ bool read_desc(const int2 *desc, TileDesc &d)
 }
 
 // ---------------------------------------------------------------- router GEMM
-// logits[T, E] = x[T, H] Wr[E, H]^T.  Workgroup: 4 waves, 64 tokens x 128
-// experts (two 16-expert column tiles per wave); grid = ceil(T/64) x ceil(E/128).
+// part[p][T, E] = x[T, Hp] Wr[E, Hp]^T over the p-th of P slices of H (kper
+// columns each).  Workgroup: 4 waves, 64 tokens x 128 experts (two 16-expert
+// column tiles per wave); grid = P x ceil(T/64) x ceil(E/128).  Splitting H
+// gives the small router enough workgroups and a short k loop each; the
+// slices are summed in a fixed order by k_pf_logits.
 __global__ __launch_bounds__(kPBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void
-k_pf_router(const f16 *__restrict__ x, const f16 *__restrict__ wr, int T, int H, int E,
-            float *__restrict__ logits)
+k_pf_router(const f16 *__restrict__ x, const f16 *__restrict__ wr, int T, int H, int E, int kper,
+            float *__restrict__ part)
 {
     constexpr int MT = kRouterRows / 16;
     constexpr int SL = stage_loads<kPWaves, MT>();
     __shared__ f16 lds[2 * kRouterRows * kLdsRow];
     const int mtiles = (T + kRouterRows - 1) / kRouterRows;
-    const int m0 = (blockIdx.x % mtiles) * kRouterRows;
-    const int c0 = (blockIdx.x / mtiles) * 128 + 32 * (threadIdx.x >> 6);
+    const int ntiles = (E + 127) / 128;
+    const int b = blockIdx.x;
+    const int m0 = (b % mtiles) * kRouterRows;
+    const int c0 = ((b / mtiles) % ntiles) * 128 + 32 * (threadIdx.x >> 6);
+    const int split = b / (mtiles * ntiles);
+    const int h0 = split * kper;
     const int t = threadIdx.x, lane = t & 63;
     const int rows = min(kRouterRows, T - m0);
     const bool active = c0 < E;
-    const f16 *brow[2] = {wr + (size_t)min(c0 + (lane & 15), E - 1) * H,
-                          wr + (size_t)min(c0 + 16 + (lane & 15), E - 1) * H};
-    f16x8 b0[2][2];
-    load_b<2>(brow, 0, lane >> 4, b0);
+    const f16 *brow[2] = {wr + (size_t)min(c0 + (lane & 15), E - 1) * H + h0,
+                          wr + (size_t)min(c0 + 16 + (lane & 15), E - 1) * H + h0};
+    f16x8 bb[kDepth + 1][2][2];
+    load_b<2>(brow, 0, lane >> 4, bb[0]);
     const uint32_t x_bytes = (uint32_t)T * H * 2;
     TokRows<SL> arows = tok_rows<SL>(x, x_bytes);
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
         const int r = t / 8 + 8 * kPWaves * i;
-        arows.off[i] = r < rows ? (uint32_t)(m0 + r) * H * 2 : x_bytes;
+        arows.off[i] = r < rows ? (uint32_t)((m0 + r) * H + h0) * 2 : x_bytes;
     }
     f32x4 acc[MT][2] = {};
-    mfma_rows<kPWaves, MT, 2>(arows, brow, H, lds, b0, acc);
+    mfma_rows<kPWaves, MT, 2, kDepth>(arows, brow, kper, lds, bb, acc);
     if (!active) return;
+    float *out = part + (size_t)split * T * E;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
         const int col = c0 + 16 * ct + (lane & 15);
@@ -250,9 +274,20 @@ k_pf_router(const f16 *__restrict__ x, const f16 *__restrict__ wr, int T, int H,
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * mt + acc_row(lane, r);
-                if (i < rows) logits[(size_t)(m0 + i) * E + col] = acc[mt][ct][r];
+                if (i < rows) out[(size_t)(m0 + i) * E + col] = acc[mt][ct][r];
             }
     }
+}
+
+// logits[i] = part[0][i] + part[1][i] + ... + part[P-1][i] (in that order).
+__global__ __launch_bounds__(256) void k_pf_logits(const float *__restrict__ part, int n, int P,
+                                                   float *__restrict__ logits)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v = part[i];
+    for (int p = 1; p < P; ++p) v += part[(size_t)p * n + i];
+    logits[i] = v;
 }
 
 // ---------------------------------------------------------------- plan
@@ -261,21 +296,36 @@ k_pf_router(const f16 *__restrict__ x, const f16 *__restrict__ wr, int T, int H,
 // shared expert (when present) is group E of both, with every token.
 // Entries with an expert id outside [0, E) are dropped (ids are a
 // precondition; this only keeps a bad id from indexing out of bounds).
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(v, off, 64);
+        if (lane >= off) v += u;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over the workgroup's threads in thread order; `total`
+// receives the sum of all.  buf: kPlanThreads / 64 ints of LDS.
 __device__ int block_exclusive_scan(int v, int *buf, int &total)
 {
-    const int t = threadIdx.x;
-    buf[t] = v;
+    constexpr int kWaves = kPlanThreads / 64;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int incl = wave_inclusive_scan(v);
+    if (lane == 63) buf[w] = incl;
     __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-        const int add = t >= off ? buf[t - off] : 0;
-        __syncthreads();
-        buf[t] += add;
-        __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int wt = buf[i];
+        if (i < w) before += wt;
+        total += wt;
     }
-    total = buf[kPlanThreads - 1];
-    const int incl = buf[t];
     __syncthreads();
-    return incl - v;
+    return before + incl - v;
 }
 
 // Descriptors of tiles tau in [0, total) for workgroups f in [0, grid): tau =
@@ -325,14 +375,23 @@ __global__ __launch_bounds__(kPlanThreads) void k_pf_plan(const int32_t *__restr
     __shared__ int cursor[kMaxExperts];
     __shared__ int ts13[kMaxExperts + 2];
     __shared__ int ts2[kMaxExperts + 2];
-    __shared__ int buf[kPlanThreads];
+    __shared__ int buf[kPlanThreads / 64];
     const int t = threadIdx.x;
     const int pairs = T * K;
     for (int e = t; e < E; e += kPlanThreads) cnt[e] = 0;
     __syncthreads();
-    for (int p = t; p < pairs; p += kPlanThreads) {
-        const int e = ids[p];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    // ids are read kPlanIds per thread at a time, all loads issued before the
+    // LDS atomics that use them
+    for (int base = 0; base < pairs; base += kPlanThreads * kPlanIds) {
+        int e[kPlanIds];
+#pragma unroll
+        for (int i = 0; i < kPlanIds; ++i) {
+            const int p = base + i * kPlanThreads + t;
+            e[i] = p < pairs ? ids[p] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < kPlanIds; ++i)
+            if ((unsigned)e[i] < (unsigned)E) atomicAdd(&cnt[e[i]], 1);
     }
     __syncthreads();
     const int c = t < E ? cnt[t] : 0;
@@ -363,17 +422,25 @@ __global__ __launch_bounds__(kPlanThreads) void k_pf_plan(const int32_t *__restr
         plan->pairs = n_pairs;
     }
     __syncthreads();
-    for (int p = t; p < pairs; p += kPlanThreads) {
-        const int e = ids[p];
-        if ((unsigned)e < (unsigned)E) perm[atomicAdd(&cursor[e], 1)] = p;
+    for (int base = 0; base < pairs; base += kPlanThreads * kPlanIds) {
+        int e[kPlanIds];
+#pragma unroll
+        for (int i = 0; i < kPlanIds; ++i) {
+            const int p = base + i * kPlanThreads + t;
+            e[i] = p < pairs ? ids[p] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < kPlanIds; ++i)
+            if ((unsigned)e[i] < (unsigned)E)
+                perm[atomicAdd(&cursor[e[i]], 1)] = base + i * kPlanThreads + t;
     }
     write_descs(ts13, groups, cnt, first, ts13[groups], grid13, desc13);
     write_descs(ts2, groups, cnt, first, ts2[groups], grid2, desc2);
 }
 
 // ---------------------------------------------------------------- W13 + SiLU
-// Tile: 128 rows of one group x 128 activation columns (8 waves); wave w owns
-// columns j = 128 n + 16 w + [0, 16): gate rows j (column tile 0) and up rows
+// Tile: 128 rows of one group x 16 kGemmWaves activation columns; wave w owns
+// columns j = 16 (kGemmWaves n + w) + [0, 16): gate rows j (column tile 0) and up rows
 // Ig + j (column tile 1), so silu(gate) * up pairs accumulator elements lane
 // by lane.  Routed expert g < E: rows are pairs p from perm, token p / K,
 // output act[p, j] (fp16, [T*K, I]).  Group E is the shared expert: rows are
@@ -397,8 +464,8 @@ k_pf_w13(const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__re
     const bool active = j0 < Ig;
     const int j = min(j0 + (lane & 15), Ig - 1);
     const f16 *brow[2] = {wbase + (size_t)j * H, wbase + (size_t)(Ig + j) * H};
-    f16x8 b0[2][2];
-    load_b<2>(brow, 0, lane >> 4, b0);
+    f16x8 bb[kDepth + 1][2][2];
+    load_b<2>(brow, 0, lane >> 4, bb[0]);
     if (t < kBM) rid[t] = t < d.rows ? (shared ? d.first + t : perm[d.first + t]) : -1;
     __syncthreads();
     const uint32_t x_bytes = (uint32_t)T * H * 2;
@@ -410,7 +477,7 @@ k_pf_w13(const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__re
         arows.off[i] = q >= 0 ? (uint32_t)(shared ? q : q / K) * H * 2 : x_bytes;
     }
     f32x4 acc[MT][2] = {};
-    mfma_rows<kGemmWaves, MT, 2>(arows, brow, H, lds, b0, acc);
+    mfma_rows<kGemmWaves, MT, 2, kDepth>(arows, brow, H, lds, bb, acc);
     if (!active) return;
     f16 *out = shared ? act_s : act;
     const int col = j0 + (lane & 15);
@@ -425,8 +492,8 @@ k_pf_w13(const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__re
 }
 
 // ---------------------------------------------------------------- W2
-// Tile: 128 rows of one group x 256 output columns h (8 waves); wave w owns
-// h = 256 n + 32 w + 16 ct + [0, 16).  Routed expert g < E:
+// Tile: 128 rows of one group x 32 kGemmWaves output columns h; wave w owns
+// h = 32 (kGemmWaves n + w) + 16 ct + [0, 16).  Routed expert g < E:
 // down[p, h] = sum_j W2[g, h, j] act[p, j] (fp32, row p of [T*K + T, H]).
 // Group E, the shared expert: down[T*K + t, h] = sum_j Wsd[h, j] act_s[t, j].
 __global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void
@@ -449,8 +516,8 @@ k_pf_w2(const f16 *__restrict__ act, const f16 *__restrict__ act_s, const f16 *_
     const bool active = c0 < H;
     const f16 *brow[2] = {wbase + (size_t)min(c0 + (lane & 15), H - 1) * kdim,
                           wbase + (size_t)min(c0 + 16 + (lane & 15), H - 1) * kdim};
-    f16x8 b0[2][2];
-    load_b<2>(brow, 0, lane >> 4, b0);
+    f16x8 bb[kDepth + 1][2][2];
+    load_b<2>(brow, 0, lane >> 4, bb[0]);
     if (t < kBM) rid[t] = t < d.rows ? (shared ? d.first + t : perm[d.first + t]) : -1;
     __syncthreads();
     const uint32_t a_bytes = shared ? (uint32_t)T * Is * 2 : (uint32_t)T * K * I * 2;
@@ -461,7 +528,7 @@ k_pf_w2(const f16 *__restrict__ act, const f16 *__restrict__ act_s, const f16 *_
         arows.off[i] = q >= 0 ? (uint32_t)q * kdim * 2 : a_bytes;
     }
     f32x4 acc[MT][2] = {};
-    mfma_rows<kGemmWaves, MT, 2>(arows, brow, kdim, lds, b0, acc);
+    mfma_rows<kGemmWaves, MT, 2, kDepth>(arows, brow, kdim, lds, bb, acc);
     if (!active) return;
     const size_t row_base = shared ? (size_t)T * K : 0;
 #pragma unroll
@@ -511,6 +578,12 @@ __global__ __launch_bounds__(256) void k_pf_combine(const float *__restrict__ do
 inline hipError_t last() { return hipGetLastError(); }
 
 constexpr int round8(long long n) { return (int)((n + 7) / 8 * 8); }
+// H slices of the router GEMM: a whole number of k steps each, at least 8,
+// at most 4 slices
+constexpr int router_split(int H)
+{
+    return (H / kBK) % 4 == 0 && H / kBK >= 32 ? 4 : (H / kBK) % 2 == 0 && H / kBK >= 16 ? 2 : 1;
+}
 constexpr int w13_col_tiles(int I) { return (I + 16 * kGemmWaves - 1) / (16 * kGemmWaves); }
 constexpr int w2_col_tiles(int H) { return (H + 32 * kGemmWaves - 1) / (32 * kGemmWaves); }
 
@@ -531,7 +604,9 @@ PrefillLayout prefill_layout(int T, int H, int E, int I, int K, int Is)
         off += align256(bytes);
         return at;
     };
+    L.router_split = router_split(H);
     L.plan = take(sizeof(PrefillPlan));
+    L.part = take((size_t)L.router_split * T * E * 4);
     L.desc13 = take((size_t)L.grid13 * 8);
     L.desc2 = take((size_t)L.grid2 * 8);
     L.perm = take((size_t)pairs * 4);
@@ -556,11 +631,16 @@ hipError_t launch_prefill(const void *x, const void *wr, const void *w13, const 
     f16 *act = reinterpret_cast<f16 *>(base + L.act);
     f16 *act_s = reinterpret_cast<f16 *>(base + L.act_s);
     float *down = reinterpret_cast<float *>(base + L.down);
-    const int router_tiles = (T + kRouterRows - 1) / kRouterRows * ((E + 127) / 128);
+    const int P = L.router_split;
+    const int router_tiles = P * ((T + kRouterRows - 1) / kRouterRows) * ((E + 127) / 128);
+    float *part = reinterpret_cast<float *>(base + L.part);
     hipError_t err = hipSuccess;
     if (stage == 0 || stage == 1) {
         hipLaunchKernelGGL(k_pf_router, dim3(router_tiles), dim3(kPBlock), 0, s,
-                           (const f16 *)x, (const f16 *)wr, T, H, E, logits);
+                           (const f16 *)x, (const f16 *)wr, T, H, E, H / P, part);
+        if ((err = last()) != hipSuccess) return err;
+        hipLaunchKernelGGL(k_pf_logits, dim3((T * E + 255) / 256), dim3(256), 0, s, part, T * E, P,
+                           logits);
         if ((err = last()) != hipSuccess) return err;
     }
     if (stage == 0 || stage == 2) {

@@ -1,4 +1,5 @@
-"""One decode layer's buffers and call sequence, and a hipGraph of many layers.
+"""One layer's buffers and call sequence (decode, or prefill over many tokens),
+and a hipGraph of many layers.
 
 A layer runs either as moe_layer_decode (three launches at M = 1) or as the
 three entry points on one stream: shared_expert (independent of routing, so it
@@ -12,7 +13,8 @@ from __future__ import annotations
 
 import torch
 
-from .api import moe_decode_fused, moe_layer_decode, moe_route, shared_expert, workspace
+from .api import (moe_dbg_prefill_stage, moe_decode_fused, moe_layer_decode, moe_layer_prefill,
+                  moe_route, prefill_workspace, shared_expert, workspace)
 from .synth import LayerShape
 
 
@@ -56,6 +58,37 @@ class DecodeLayer:
         return self.y
 
 
+class PrefillLayer:
+    """One layer over T = shape.M tokens through moe_layer_prefill, with
+    preallocated outputs; `ws` may be shared by layers that run one after
+    another on one stream (the workspace holds nothing between calls)."""
+
+    def __init__(self, tensors: dict, shape: LayerShape, ws=None):
+        self.shape = shape
+        self.t = tensors
+        dev = tensors["x"].device
+        T, H, E, K = shape.M, shape.H, shape.E, shape.K
+        self.topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, K), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+        self.y = torch.empty((T, H), dtype=torch.float16, device=dev)
+        self.ws = ws if ws is not None else prefill_workspace(max(T, 1), H, E, shape.I, K,
+                                                              shape.Is, dev)
+
+    def _args(self):
+        t, sh = self.t, self.shape
+        return (t["x"], t["wr"], t["w13"], t["w2"], t["wsgu"], t["wsd"], sh.K, sh.renormalize,
+                self.topk_ids, self.topk_w, self.logits, self.y, self.ws)
+
+    def forward(self, stream=None):
+        moe_layer_prefill(*self._args(), stream=stream)
+        return self.y
+
+    def stage(self, stage: int, stream=None):
+        """One of the six stages alone (1..6), reading what earlier ones left."""
+        moe_dbg_prefill_stage(stage, *self._args(), stream=stream)
+
+
 class DecodeStack:
     """Layers run in sequence; capture() records them into one hipGraph."""
 
@@ -68,6 +101,8 @@ class DecodeStack:
             layer.forward(stream)
 
     def capture(self):
+        """Record every layer's launches into one hipGraph (works for decode and
+        prefill layers alike)."""
         dev = self.layers[0].y.device
         side = torch.cuda.Stream(device=dev)
         side.wait_stream(torch.cuda.current_stream(dev))
