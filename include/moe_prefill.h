@@ -2,7 +2,7 @@
  * moe_prefill.h -- C ABI of the many-token (prefill) MoE layer on MI355X
  * (gfx950): the layer of moe_decode.h (router, top-K + softmax, routed
  * gate/up + SiLU*mul, down + weighted combine, shared expert), for T tokens
- * at once, with each expert's weights read once per tile of up to 64 of the
+ * at once, with each expert's weights read once per tile of up to 128 of the
  * tokens routed to it and the products on the matrix cores.
  *
  * Where the pages define it: "如何在天垓 BI-V100 上优化大模型推理：一份工作

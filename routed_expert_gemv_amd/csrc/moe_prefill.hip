@@ -8,18 +8,22 @@
 // per-expert loop by one grouped GEMM).  Design for CDNA4:
 //   * one workgroup groups the (token, slot) pairs by expert and writes a list
 //     of tiles; every expert's weight rows are then streamed from HBM once per
-//     tile of up to 64 of its tokens (tiles of one expert are placed on one XCD
-//     so a second tile's re-read is served by that XCD's L2);
+//     tile of up to 128 of its tokens (tiles of one expert are placed on one
+//     XCD so a second tile's re-read can be served by that XCD's L2);
 //   * the products run on the matrix cores, v_mfma_f32_16x16x32_f16 (fp16
 //     inputs, fp32 accumulators).  The weight operand goes from HBM straight
 //     into registers in the instruction's operand layout: one load instruction
 //     reads 64 contiguous bytes from each of 16 weight rows (16 whole 64-byte
-//     sectors per 1 KiB).  The token operand is staged in LDS once per
-//     workgroup with a 144-byte row stride, which keeps the 16-byte fragment
-//     reads free of bank conflicts;
+//     sectors per 1 KiB), two k steps ahead of its products.  The token
+//     operand is read through buffer loads (padding rows of a partly filled
+//     tile read nothing) and staged in LDS once per workgroup with a 144-byte
+//     row stride, which keeps the 16-byte fragment reads free of bank
+//     conflicts;
 //   * gate row j and up row I + j sit in accumulator tiles of the same wave at
 //     the same lane positions, so SiLU(gate) * up is formed in registers and
 //     stored once (fp16);
+//   * the router is a GEMM over slices of H (enough workgroups for its small
+//     weight), summed in a fixed order;
 //   * the shared expert is one more group of both grouped GEMMs (every token);
 //     the down products are written per (token, slot) in fp32 and a last pass
 //     sums them with the routing weights in routing order, adds the shared
@@ -50,8 +54,6 @@ constexpr int kDepth = 2;               // k steps in flight in the GEMM main lo
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanIds = 16;            // expert ids per plan thread per pass
-
-__device__ __forceinline__ f16x8 ld16(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
 
 __device__ __forceinline__ f16x8 ld16_stream(const f16 *p)
 {
