@@ -31,6 +31,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
+// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family GPUs.
+constexpr int kBufferWord3 = 0x00020000;
 constexpr int kBlock = kWave * kWavesPerBlock;
 
 // ---------------------------------------------------------------- helpers
@@ -317,6 +319,16 @@ __global__ __launch_bounds__(kWave) void k_topk(const float *__restrict__ logits
     }
 }
 
+// Slot (top-k index) of token m in distinct-expert entry u: the entry's 8
+// slot bytes are read with one 8-byte load at a uniform address, which the
+// compiler issues as a scalar load.  (Reading the byte alone becomes a vector
+// byte load, and waiting for it also waits for every weight load in flight.)
+__device__ __forceinline__ int table_slot(const GroupTable *__restrict__ table, int u, int m)
+{
+    const uint64_t row = *reinterpret_cast<const uint64_t *>(table->u_slot[u]);
+    return (int)(signed char)(uint8_t)(row >> (8 * m));
+}
+
 // ---------------------------------------------------------------- W13 + SiLU
 // One wave per (expert, row pair j): gate row j and up row I + j of that
 // expert, read in place at W13 + expert*(2I*H).  Both rows are loaded before
@@ -396,7 +408,7 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
         expert = table->u_expert[u];
         mask = table->u_mask[u];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) slot[m] = table->u_slot[u][m];
+        for (int m = 0; m < MT; ++m) slot[m] = table_slot(table, u, m);
     }
     const f16 *base = w13 + (size_t)expert * 2 * I * H;
     f16x8 wg[2][HC], wu[2][HC];
@@ -428,21 +440,35 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
     }
     __syncthreads();
 
+    // Results stay in registers until every row pair is consumed: a store
+    // under the token-mask branch would leave the compiler unsure how many
+    // memory operations are outstanding, and it would then wait for all of
+    // them (the prefetched row pair included) before the next product.
+    float res[kRowsPerWaveM][MT];
 #pragma unroll
     for (int i = 0; i < kRowsPerWaveM; ++i) {
         const int buf = i & 1;
         if (i + 1 < kRowsPerWaveM) load_pair(i + 1, buf ^ 1);
-        const int j = j0 + i * kWavesPerBlock;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m) {
+            res[i][m] = 0.0f;
             if (mask & (1u << m)) {
                 f16x8 xv[HC];
 #pragma unroll
                 for (int c = 0; c < HC; ++c) xv[c] = xs[(m * HC + c) * kWave + lane];
                 const float g = row_dot<HC>(wg[buf], xv);
                 const float up = row_dot<HC>(wu[buf], xv);
-                if (lane == 0) act[((size_t)m * K + slot[m]) * I + j] = silu_mul(g, up);
+                res[i][m] = silu_mul(g, up);
             }
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < kRowsPerWaveM; ++i)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                if (mask & (1u << m))
+                    act[((size_t)m * K + slot[m]) * I + j0 + i * kWavesPerBlock] = res[i][m];
     }
 }
 
@@ -531,7 +557,7 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
                         int k;
                         if (SHARED) k = 0;
                         else if (MT == 1) k = u0 + t;
-                        else k = table->u_slot[u0 + t][m];
+                        else k = table_slot(table, u0 + t, m);
                         const float wt = SHARED ? 1.0f : topk_w[(size_t)m * K + k];
                         const float *a = act + ((size_t)m * (SHARED ? 1 : K) + k) * I;
                         float d = 0.0f;
@@ -590,21 +616,43 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     const int n_u = SHARED ? 1 : table->n_u;
 
     // two batches of W2 rows: the next batch is requested before the current
-    // one is combined
+    // one is combined.  Every load is issued (none under a branch, so the
+    // compiler waits for exactly the batch it combines): a slot past the last
+    // distinct expert reads through a zero-sized buffer range, which returns
+    // zeros and touches no memory.  Each batch's table entries (expert ids,
+    // token masks, slot bytes) are read with it, as scalar loads at uniform
+    // addresses, so the combine waits on nothing but that batch.
     f16x8 wv[2][BATCH][CPL];
+    unsigned bmask[2][BATCH];
+    uint64_t bslot[2][BATCH];
     auto load_batch = [&](int buf, int u0) {
-        const int cnt = n_u - u0 < BATCH ? n_u - u0 : BATCH;
+        const int ub = u0 < kMaxSlots - BATCH ? u0 : kMaxSlots - BATCH; // entries stay in the table
+        int ids[BATCH];
 #pragma unroll
-        for (int t = 0; t < BATCH; ++t)
-            if (t < cnt) {
-                const int e = SHARED ? 0 : table->u_expert[u0 + t];
-                const f16x8 *row = reinterpret_cast<const f16x8 *>(w2 + ((size_t)e * H + h) * I);
+        for (int t = 0; t < BATCH; ++t) {
+            ids[t] = SHARED ? 0 : table->u_expert[ub + t];
+            bmask[buf][t] = SHARED ? (1u << M) - 1u : table->u_mask[ub + t];
+            bslot[buf][t] = SHARED ? 0 : *reinterpret_cast<const uint64_t *>(table->u_slot[ub + t]);
+        }
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) wv[buf][t][c] = stream_load(row + c * LPR + cl);
-            }
+        for (int t = 0; t < BATCH; ++t) {
+            const bool ok = u0 + t < n_u;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<f16 *>(w2) + (size_t)(ok ? ids[t] : 0) * H * I, (short)0,
+                ok ? H * I * 2 : 0, kBufferWord3);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+                wv[buf][t][c] = __builtin_bit_cast(
+                    f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                               rs, (uint32_t)(h * I + (c * LPR + cl) * 8) * 2, 0, 0));
+        }
     };
     load_batch(0, 0);
 
+    // routing weights [M, K] into LDS (read per expert and token by the combine)
+    __shared__ float s_tw[kMaxSlots];
+    if (!SHARED)
+        for (int i = threadIdx.x; i < M * K; i += kSBlock) s_tw[i] = topk_w[i];
     // stage act: 16-byte chunks, 4 in flight per thread per step
     const int n4 = M * slots * I / 4;
     const f32x4 *a4 = reinterpret_cast<const f32x4 *>(act);
@@ -632,12 +680,12 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
 #pragma unroll
         for (int t = 0; t < BATCH; ++t)
             if (t < cnt) {
-                const unsigned mask = SHARED ? (1u << M) - 1u : table->u_mask[u0 + t];
+                const unsigned mask = bmask[buf][t];
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
                     if (mask & (1u << m)) {
-                        const int k = SHARED ? 0 : table->u_slot[u0 + t][m];
-                        const float wt = SHARED ? 1.0f : topk_w[(size_t)m * K + k];
+                        const int k = (int)(signed char)(uint8_t)(bslot[buf][t] >> (8 * m));
+                        const float wt = SHARED ? 1.0f : s_tw[m * K + k];
                         const float *a = lds + ((size_t)m * slots + k) * I;
                         float d = 0.0f;
 #pragma unroll
@@ -650,12 +698,10 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
             }
     };
     for (int u0 = 0; u0 < n_u; u0 += 2 * BATCH) {
-        if (u0 + BATCH < n_u) load_batch(1, u0 + BATCH);
+        load_batch(1, u0 + BATCH);
         combine(0, u0);
-        if (u0 + BATCH < n_u) {
-            if (u0 + 2 * BATCH < n_u) load_batch(0, u0 + 2 * BATCH);
-            combine(1, u0 + BATCH);
-        }
+        load_batch(0, u0 + 2 * BATCH);
+        combine(1, u0 + BATCH);
     }
 
     const bool holder = lane == group_holder<LPR>(r);
@@ -1226,16 +1272,21 @@ static hipError_t launch_w2_t(const float *act, const void *w2, const int32_t *i
         // several tokens: stage the activations in LDS when they fit
         const size_t lds = (size_t)M * (SHARED ? 1 : K) * I * sizeof(float);
         constexpr int rows = (kWave / LPR) * kSWaves;
-        if (H % rows == 0 && lds <= lds_optin_bytes()) {
+        // the kernel's static LDS (routing weights) comes on top of `lds`
+        if (H % rows == 0 && lds + kMaxSlots * sizeof(float) <= lds_optin_bytes()) {
             auto kern = k_w2_staged<LPR, CPL, MT, SHARED>;
             // opt this instance into the device's full LDS, once per device
             static bool opted[kMaxDevices] = {};
             int dev = 0;
             if (lds > 64 * 1024 && hipGetDevice(&dev) == hipSuccess && dev < kMaxDevices &&
                 !opted[dev]) {
-                const hipError_t e = hipFuncSetAttribute(
-                    reinterpret_cast<const void *>(kern),
-                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_optin_bytes());
+                // dynamic LDS may use what the kernel's static LDS leaves
+                hipFuncAttributes fa;
+                hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
+                if (e != hipSuccess) return e;
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)(lds_optin_bytes() - fa.sharedSizeBytes));
                 if (e != hipSuccess) return e;
                 opted[dev] = true;
             }
