@@ -1040,8 +1040,10 @@ __global__ __launch_bounds__(kBlock) void k_route_shared_m(const f16 *__restrict
                                   xs);
 }
 
+constexpr int kSelBlock = kMaxTokens * kWave; // one wave per token
+
 template <int NPL>
-__global__ __launch_bounds__(kBlock) void k_select_m(const float *__restrict__ logits, int M,
+__global__ __launch_bounds__(kSelBlock) void k_select_m(const float *__restrict__ logits, int M,
                                                      int E, int K, int renormalize,
                                                      int32_t *__restrict__ ids,
                                                      float *__restrict__ weights,
@@ -1051,7 +1053,7 @@ __global__ __launch_bounds__(kBlock) void k_select_m(const float *__restrict__ l
     __shared__ int32_t sids[kMaxSlots];
     const int wave = threadIdx.x / kWave;
     const int lane = lane_id();
-    for (int m = wave; m < M; m += kWavesPerBlock) { // the top-k kernel's work, token m
+    for (int m = wave; m < M; m += kMaxTokens) { // the top-k kernel's work, token m
         const float *L = logits + (size_t)m * E;
         float v[NPL];
 #pragma unroll
@@ -1541,13 +1543,13 @@ static hipError_t launch_lean_m_t(const void *x, const void *wr, const void *w13
     hipError_t err = last();
     if (err != hipSuccess) return err;
     if (E <= kWave)
-        hipLaunchKernelGGL(k_select_m<1>, dim3(1), dim3(kBlock), 0, s, logits, M, E, K, renorm,
+        hipLaunchKernelGGL(k_select_m<1>, dim3(1), dim3(kSelBlock), 0, s, logits, M, E, K, renorm,
                            ids, w, table);
     else if (E <= 4 * kWave)
-        hipLaunchKernelGGL(k_select_m<4>, dim3(1), dim3(kBlock), 0, s, logits, M, E, K, renorm,
+        hipLaunchKernelGGL(k_select_m<4>, dim3(1), dim3(kSelBlock), 0, s, logits, M, E, K, renorm,
                            ids, w, table);
     else
-        hipLaunchKernelGGL(k_select_m<kMaxExperts / kWave>, dim3(1), dim3(kBlock), 0, s, logits,
+        hipLaunchKernelGGL(k_select_m<kMaxExperts / kWave>, dim3(1), dim3(kSelBlock), 0, s, logits,
                            M, E, K, renorm, ids, w, table);
     if ((err = last()) != hipSuccess) return err;
     const int n_slots = M * K < E ? M * K : E;
