@@ -619,21 +619,16 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     // one is combined.  Every load is issued (none under a branch, so the
     // compiler waits for exactly the batch it combines): a slot past the last
     // distinct expert reads through a zero-sized buffer range, which returns
-    // zeros and touches no memory.  Each batch's table entries (expert ids,
-    // token masks, slot bytes) are read with it, as scalar loads at uniform
-    // addresses, so the combine waits on nothing but that batch.
+    // zeros and touches no memory.  Each batch's expert ids are read with it
+    // (scalar loads at uniform addresses); the token masks and slot bytes the
+    // combine needs are staged in LDS with the activations, so the combine
+    // waits on nothing but its batch.
     f16x8 wv[2][BATCH][CPL];
-    unsigned bmask[2][BATCH];
-    uint64_t bslot[2][BATCH];
     auto load_batch = [&](int buf, int u0) {
         const int ub = u0 < kMaxSlots - BATCH ? u0 : kMaxSlots - BATCH; // entries stay in the table
         int ids[BATCH];
 #pragma unroll
-        for (int t = 0; t < BATCH; ++t) {
-            ids[t] = SHARED ? 0 : table->u_expert[ub + t];
-            bmask[buf][t] = SHARED ? (1u << M) - 1u : table->u_mask[ub + t];
-            bslot[buf][t] = SHARED ? 0 : *reinterpret_cast<const uint64_t *>(table->u_slot[ub + t]);
-        }
+        for (int t = 0; t < BATCH; ++t) ids[t] = SHARED ? 0 : table->u_expert[ub + t];
 #pragma unroll
         for (int t = 0; t < BATCH; ++t) {
             const bool ok = u0 + t < n_u;
@@ -649,10 +644,17 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     };
     load_batch(0, 0);
 
-    // routing weights [M, K] into LDS (read per expert and token by the combine)
+    // routing weights [M, K], the distinct experts' token masks and slot
+    // bytes into LDS (read per expert and token by the combine)
     __shared__ float s_tw[kMaxSlots];
+    __shared__ unsigned s_mask[kMaxSlots];
+    __shared__ uint64_t s_slot[kMaxSlots];
     if (!SHARED)
-        for (int i = threadIdx.x; i < M * K; i += kSBlock) s_tw[i] = topk_w[i];
+        for (int i = threadIdx.x; i < kMaxSlots; i += kSBlock) {
+            if (i < M * K) s_tw[i] = topk_w[i];
+            s_mask[i] = table->u_mask[i];
+            s_slot[i] = *reinterpret_cast<const uint64_t *>(table->u_slot[i]);
+        }
     // stage act: 16-byte chunks, 4 in flight per thread per step
     const int n4 = M * slots * I / 4;
     const f32x4 *a4 = reinterpret_cast<const f32x4 *>(act);
@@ -680,11 +682,12 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
 #pragma unroll
         for (int t = 0; t < BATCH; ++t)
             if (t < cnt) {
-                const unsigned mask = bmask[buf][t];
+                const unsigned mask = SHARED ? (1u << M) - 1u : s_mask[u0 + t];
+                const uint64_t slot8 = SHARED ? 0 : s_slot[u0 + t];
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
                     if (mask & (1u << m)) {
-                        const int k = (int)(signed char)(uint8_t)(bslot[buf][t] >> (8 * m));
+                        const int k = (int)(signed char)(uint8_t)(slot8 >> (8 * m));
                         const float wt = SHARED ? 1.0f : s_tw[m * K + k];
                         const float *a = lds + ((size_t)m * slots + k) * I;
                         float d = 0.0f;
@@ -1274,8 +1277,9 @@ static hipError_t launch_w2_t(const float *act, const void *w2, const int32_t *i
         // several tokens: stage the activations in LDS when they fit
         const size_t lds = (size_t)M * (SHARED ? 1 : K) * I * sizeof(float);
         constexpr int rows = (kWave / LPR) * kSWaves;
-        // the kernel's static LDS (routing weights) comes on top of `lds`
-        if (H % rows == 0 && lds + kMaxSlots * sizeof(float) <= lds_optin_bytes()) {
+        // the kernel's static LDS (routing weights, table masks and slots)
+        // comes on top of `lds`
+        if (H % rows == 0 && lds + kMaxSlots * 16 <= lds_optin_bytes()) {
             auto kern = k_w2_staged<LPR, CPL, MT, SHARED>;
             // opt this instance into the device's full LDS, once per device
             static bool opted[kMaxDevices] = {};

@@ -215,6 +215,9 @@ def test_prefill_workspace_bytes():
     assert L.moe_prefill_workspace_bytes(T, H, E, I, K, 32) == 0         # Is % 64
     assert L.moe_prefill_workspace_bytes(T, H, 1025, I, K, Is) == 0      # E
     assert L.moe_prefill_workspace_bytes(T, H, 4, I, 8, Is) == 0         # K > E
+    # routed activations [T*K, I] fp16 must stay under 4 GiB (32-bit row offsets)
+    assert L.moe_prefill_workspace_bytes(65536, 1024, 256, 2048, 16, 0) == 0
+    assert L.moe_prefill_workspace_bytes(65536, 1024, 256, 1024, 16, 0) > 0
     assert L.moe_prefill_workspace_bytes(T, 64, 16, 64, 4, 64) > 0       # smallest dims
 
 
