@@ -17,7 +17,9 @@
  *   - sizes (MOE_ERR_SHAPE otherwise): 0 <= T <= 65536; H a multiple of 64 in
  *     [64, 16384]; 1 <= E <= 1024; 1 <= K <= min(E, 16); I a multiple of 64 in
  *     [64, 4096]; Is = 0 (no shared expert) or a multiple of 64 in [64, 4096];
- *   - T = 0 is a valid empty call.
+ *   - T = 0 is a valid empty call;
+ *   - alignment (MOE_ERR_ALIGN otherwise): as moe_decode.h, except that y must
+ *     be 8-byte aligned (it is written four halves at a time).
  */
 #ifndef MOE_PREFILL_H
 #define MOE_PREFILL_H

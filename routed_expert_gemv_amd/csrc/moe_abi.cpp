@@ -51,8 +51,9 @@ static moe_status layer_prefill(const void *x, const void *w_router, const void 
     if (!x || !w_router || !w13 || !w2 || !topk_ids || !topk_w || !logits || !y || !ws ||
         (shared && (!w_gate_up || !w_down)))
         return MOE_ERR_NULL;
+    // y is written four halves (8 bytes) at a time
     if (!al(x, 16) || !al(w_router, 16) || !al(w13, 16) || !al(w2, 16) || !al(topk_ids, 4) ||
-        !al(topk_w, 4) || !al(logits, 4) || !al(y, 2) || !al(ws, 256) ||
+        !al(topk_w, 4) || !al(logits, 4) || !al(y, 8) || !al(ws, 256) ||
         (shared && (!al(w_gate_up, 16) || !al(w_down, 16))))
         return MOE_ERR_ALIGN;
     if (ws_bytes < prefill_layout(T, H, E, I, K, Is).bytes) return MOE_ERR_WORKSPACE;

@@ -244,6 +244,7 @@ def test_prefill_validation():
     assert call(Is=0) == -2               # shared weights given but Is = 0
     assert call(w13=FAKE_ODD) == -3
     assert call(ws=FAKE + 16) == -3
+    assert call(y=FAKE + 4) == -3         # y is written 8 bytes at a time
     assert call(n=need - 1) == -4
     assert call(T=0) == 0                 # empty call: nothing enqueued
     # without a shared expert Is is ignored and the workspace is smaller
