@@ -150,6 +150,23 @@ def cpu_baseline(stack_tensors, sh, budget_s=12.0):
                       "router, top-k, 8 experts, shared expert), %.1f s wall" % (done, el)}
 
 
+def replay_percentiles(stack, n, layers):
+    """p10 / p50 / p90 of the per-layer time over n replays, each bracketed by
+    its own pair of HIP events (after the timed loop, so it does not perturb it)."""
+    import torch
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        stack.replay()
+        b.record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 / layers for a, b in ev)
+    pick = lambda q: round(us[min(len(us) - 1, int(q * (len(us) - 1) + 0.5))], 3)
+    return [pick(0.1), pick(0.5), pick(0.9)]
+
+
 def time_stages(layers, reps):
     """Average duration of each of the three kernels of a layer: for each kernel,
     a hipGraph of that kernel alone for every layer of the stack (inputs left
@@ -277,6 +294,7 @@ def prefill_main(args, dev):
     torch.cuda.synchronize()
     ms_step = a.elapsed_time(b) / args.steps
     us_layer = ms_step * 1e3 / n_layers
+    pct = replay_percentiles(stack, args.steps, n_layers)
     n_distinct = [len(set(l.topk_ids.flatten().tolist())) for l in layers]
     nd = sum(n_distinct) / len(n_distinct)
     w_bytes = nd * 3 * 2 * sh.I * sh.H + 3 * 2 * sh.Is * sh.H + 2 * sh.E * sh.H
@@ -309,6 +327,7 @@ def prefill_main(args, dev):
                    "tokens": T, "layers": n_layers, "layer_seeds": "0..%d" % (n_layers - 1),
                    "distinct_experts_per_layer": round(nd, 2)},
         "us_per_layer": round(us_layer, 3),
+        "us_per_layer_p10_p50_p90": pct,
         "weight_gbs": round(w_bytes / (us_layer * 1e-6) / 1e9, 1),
         "frac_of_peak": round(w_bytes / (us_layer * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,
@@ -601,6 +620,7 @@ def main():
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
     us_layer = ms_step * 1e3 / args.layers
+    pct = replay_percentiles(stack, args.steps, args.layers)
 
     n_distinct = [len(set(l.topk_ids.flatten().tolist())) for l in layers]
     expert_b = sum(layer_bytes(sh, n)[0] for n in n_distinct)
@@ -639,6 +659,7 @@ def main():
                    "layers": args.layers, "layer_seeds": "0..%d" % (args.layers - 1),
                    "path": args.path},
         "us_per_layer": round(us_layer, 3),
+        "us_per_layer_p10_p50_p90": pct,
         "frac_of_peak": round(gbs_expert / HBM_PEAK_GBS, 4),
         "gbs_total": round(gbs_total, 1),
         "expert_bytes_per_layer": expert_b // args.layers,
