@@ -42,8 +42,8 @@ typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPWaves = 4;
-constexpr int kPBlock = 64 * kPWaves;
+constexpr int kRouterWaves = 4;            // waves per router workgroup
+constexpr int kRouterBlock = 64 * kRouterWaves;
 constexpr int kBM = kPrefillRows;       // token rows per grouped-GEMM tile: eight 16-row MFMA tiles
 constexpr int kBK = 64;                 // k per main-loop step (two 32-wide MFMA steps)
 constexpr int kLdsRow = kBK + 8;        // halves per staged row (144 bytes)
@@ -235,12 +235,12 @@ __device__ __forceinline__ bool read_desc(const int2 *desc, TileDesc &d)
 // column tiles per wave); grid = P x ceil(T/64) x ceil(E/128).  Splitting H
 // gives the small router enough workgroups and a short k loop each; the
 // slices are summed in a fixed order by k_pf_logits.
-__global__ __launch_bounds__(kPBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+__global__ __launch_bounds__(kRouterBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 k_pf_router(const f16 *__restrict__ x, const f16 *__restrict__ wr, int T, int H, int E, int kper,
             float *__restrict__ part)
 {
     constexpr int MT = kRouterRows / 16;
-    constexpr int SL = stage_loads<kPWaves, MT>();
+    constexpr int SL = stage_loads<kRouterWaves, MT>();
     __shared__ f16 lds[2 * kRouterRows * kLdsRow];
     const int mtiles = (T + kRouterRows - 1) / kRouterRows;
     const int ntiles = (E + 127) / 128;
@@ -260,11 +260,11 @@ k_pf_router(const f16 *__restrict__ x, const f16 *__restrict__ wr, int T, int H,
     TokRows<SL> arows = tok_rows<SL>(x, x_bytes);
 #pragma unroll
     for (int i = 0; i < SL; ++i) {
-        const int r = t / 8 + 8 * kPWaves * i;
+        const int r = t / 8 + 8 * kRouterWaves * i;
         arows.off[i] = r < rows ? (uint32_t)((m0 + r) * H + h0) * 2 : x_bytes;
     }
     f32x4 acc[MT][2] = {};
-    mfma_rows<kPWaves, MT, 2, kDepth>(arows, brow, kper, lds, bb, acc);
+    mfma_rows<kRouterWaves, MT, 2, kDepth>(arows, brow, kper, lds, bb, acc);
     if (!active) return;
     float *out = part + (size_t)split * T * E;
 #pragma unroll
@@ -293,11 +293,6 @@ __global__ __launch_bounds__(256) void k_pf_logits(const float *__restrict__ par
 }
 
 // ---------------------------------------------------------------- plan
-// One workgroup: counts the (token, slot) pairs of each expert, lists them
-// expert by expert (perm), and writes the W13 and W2 tile descriptors; the
-// shared expert (when present) is group E of both, with every token.
-// Entries with an expert id outside [0, E) are dropped (ids are a
-// precondition; this only keeps a bad id from indexing out of bounds).
 __device__ __forceinline__ int wave_inclusive_scan(int v)
 {
     const int lane = threadIdx.x & 63;
@@ -363,6 +358,11 @@ __device__ void write_descs(const int *ts, int ngroups, const int *rows_of, cons
     }
 }
 
+// One workgroup: counts the (token, slot) pairs of each expert, lists them
+// expert by expert (perm), and writes the W13 and W2 tile descriptors; the
+// shared expert (when present) is group E of both, with every token.
+// Entries with an expert id outside [0, E) are dropped (ids are a
+// precondition; this only keeps a bad id from indexing out of bounds).
 __global__ __launch_bounds__(kPlanThreads) void k_pf_plan(const int32_t *__restrict__ ids, int T,
                                                           int K, int E, int nt13, int nt13_shared,
                                                           int nt2, int shared, int grid13,
@@ -638,7 +638,7 @@ hipError_t launch_prefill(const void *x, const void *wr, const void *w13, const 
     float *part = reinterpret_cast<float *>(base + L.part);
     hipError_t err = hipSuccess;
     if (stage == 0 || stage == 1) {
-        hipLaunchKernelGGL(k_pf_router, dim3(router_tiles), dim3(kPBlock), 0, s,
+        hipLaunchKernelGGL(k_pf_router, dim3(router_tiles), dim3(kRouterBlock), 0, s,
                            (const f16 *)x, (const f16 *)wr, T, H, E, H / P, part);
         if ((err = last()) != hipSuccess) return err;
         hipLaunchKernelGGL(k_pf_logits, dim3((T * E + 255) / 256), dim3(256), 0, s, part, T * E, P,
