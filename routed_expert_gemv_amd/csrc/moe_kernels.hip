@@ -726,14 +726,18 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
 // ---------------------------------------------------------------- layer path (M = 1)
 // Three launches for a whole layer at M = 1, plain grids of independent
 // workgroups (the kernel boundaries are the only hand-offs):
-//   k_router_shared  router rows -> logits; shared gate/up rows -> SiLU*mul
-//                    activations (routing-independent bytes that stream in the
-//                    router's latency shadow)
+//   k_router1        router rows -> logits, one single-wave workgroup per row
 //   k_expand         each routed workgroup selects the experts from the logits
 //                    itself, then its gate/up rows of the selected expert ->
-//                    activations; the shared down rows -> s (fp32)
-//   k_reduce         routed down rows with the weighted combine, + s, the one
-//                    fp16 rounding
+//                    activations; the shared gate/up rows -> SiLU*mul
+//                    activations (routing-independent bytes that stream while
+//                    the routed workgroups select)
+//   k_reduce         routed down rows with the weighted combine, the shared
+//                    down rows, the one fp16 rounding
+// That placement needs the shared down projection to use the routed one's
+// lane mapping (Is == I).  For any other shared width the shared gate/up rows
+// stream beside the router (k_router_shared) and the shared down rows in
+// k_expand (-> s, fp32), which k_reduce adds.
 // The per-element arithmetic is the separate kernels' (the same device
 // functions, lane mappings and reduction trees, in the same order), so the
 // results equal shared_expert + moe_route + moe_decode_fused bit for bit.
@@ -757,6 +761,23 @@ __device__ __forceinline__ float w13_pair(const f16 *__restrict__ x, const f16 *
     const float g = row_dot<HC>(wg, xv);
     const float up = row_dot<HC>(wu, xv);
     return silu_mul(g, up);
+}
+
+// One single-wave workgroup per router row (the router kernel's arithmetic):
+// a layer's router is latency-bound, and 256 small workgroups spread its rows
+// over every CU.
+template <int HC>
+__global__ __launch_bounds__(kWave) void k_router1(const f16 *__restrict__ x,
+                                                   const f16 *__restrict__ wr,
+                                                   float *__restrict__ logits)
+{
+    constexpr int H = 512 * HC;
+    const int e = blockIdx.x;
+    f16x8 w[HC], xv[HC];
+    load_row<HC>(wr + (size_t)e * H, w);
+    load_x<HC>(x, xv);
+    const float t = row_dot<HC>(w, xv);
+    if (lane_id() == 0) logits[e] = t;
 }
 
 // Workgroups [0, ceil(E/4)): one wave per router row (the router kernel's
@@ -786,18 +807,25 @@ __global__ __launch_bounds__(kBlock) void k_router_shared(const f16 *__restrict_
     }
 }
 
+// Shared-expert work placed in the expand launch.
+enum : int { kExpandNoShared = 0, kExpandSharedDown = 1, kExpandSharedGateUp = 2 };
+
 // Routed workgroups [0, K*I/4) take (slot u, row pair j).  Wave 0 selects
 // from the logits only as far as it needs: u + 1 rounds of the top-k give slot
 // u's expert (the rounds are the top-k kernel's), so the workgroups of early
 // slots start streaming sooner.  The first workgroup of the last slot runs all
 // K rounds and also writes ids and weights (the top-k kernel's arithmetic).
-// Shared workgroups: one wave per RPL = 64/LPR rows of the shared down
-// projection (the W2 kernel's arithmetic with weight 1), s[h] in fp32.
-template <int HC, int NPL, int LPR, int CPL>
+// The workgroups after them (SM):
+//   kExpandSharedGateUp  one wave per shared gate/up row pair (wsh = the
+//                        shared gate/up weights) -> act_s;
+//   kExpandSharedDown    one wave per RPL = 64/LPR rows of the shared down
+//                        projection (wsh = the shared down weights; the W2
+//                        kernel's arithmetic with weight 1) -> s (fp32).
+template <int HC, int NPL, int LPR, int CPL, int SM>
 __global__ __launch_bounds__(kBlock) void k_expand(
-    const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsd,
-    const float *__restrict__ logits, const float *__restrict__ act_s, int E, int I, int K,
-    int Is, int renormalize, int32_t *__restrict__ ids, float *__restrict__ weights,
+    const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsh,
+    const float *__restrict__ logits, float *__restrict__ act_s, int E, int I, int K, int Is,
+    int renormalize, int32_t *__restrict__ ids, float *__restrict__ weights,
     float *__restrict__ act, float *__restrict__ s_out)
 {
     constexpr int H = 512 * HC;
@@ -830,12 +858,16 @@ __global__ __launch_bounds__(kBlock) void k_expand(
         const int j = (b % per_expert) * kWavesPerBlock + wave;
         const float a = w13_pair<HC>(x, w13 + (size_t)sh_id * 2 * I * H, I, j);
         if (lane == 0) act[(size_t)u * I + j] = a;
-    } else {
+    } else if constexpr (SM == kExpandSharedGateUp) {
+        const int j = (b - routed_blocks) * kWavesPerBlock + wave;
+        const float a = w13_pair<HC>(x, wsh, Is, j);
+        if (lane == 0) act_s[j] = a;
+    } else if constexpr (SM == kExpandSharedDown) {
         constexpr int RPL = kWave / LPR;
         const int r = lane / LPR;
         const int cl = lane % LPR;
         const int h = ((b - routed_blocks) * kWavesPerBlock + wave) * RPL + r;
-        const f16x8 *row = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * Is);
+        const f16x8 *row = reinterpret_cast<const f16x8 *>(wsh + (size_t)h * Is);
         f16x8 wv[CPL];
 #pragma unroll
         for (int c = 0; c < CPL; ++c) wv[c] = stream_load(row + c * LPR + cl);
@@ -857,20 +889,28 @@ __global__ __launch_bounds__(kBlock) void k_expand(
 // the activations [K*I] in LDS, then every lane accumulates as the W2 kernel
 // does: acc += w[k] * (its part of row h of W2[e_k] . act_k), experts in
 // routing order; one group reduction; y = fp16(acc + s[h]).
+// SH: the shared down projection is computed here too (Is == I, so its rows
+// use the same lane mapping): s[h] = the W2 kernel's arithmetic with weight 1
+// over row h of the shared down weights and act_s, added as s_in would be.
 constexpr int kRWaves = 8;
 constexpr int kRBlock = kRWaves * kWave;
 constexpr int kMaxStaged = 16384; // K*I fp32 values staged in LDS (64 KB)
 
 // STAGE: 16-byte activation loads per thread, ceil(K*I / (4 * kRBlock)).
-template <int LPR, int CPL, int STAGE>
+template <int LPR, int CPL, int STAGE, bool SH>
 __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ act,
                                                     const f16 *__restrict__ w2,
                                                     const int32_t *__restrict__ ids,
                                                     const float *__restrict__ tw,
-                                                    const float *__restrict__ s_in, int H, int I,
-                                                    int K, f16 *__restrict__ y)
+                                                    const float *__restrict__ s_in,
+                                                    const f16 *__restrict__ wsd,
+                                                    const float *__restrict__ act_s, int H,
+                                                    int I, int K, f16 *__restrict__ y)
 {
     extern __shared__ float lds[]; // [K*I] routed activations
+    // K >= 1 (checked on the host); stated so that the compiler keeps the
+    // first batch of loads ahead of the staging barrier
+    __builtin_assume(K > 0);
     constexpr int RPL = kWave / LPR;
     constexpr int BATCH = 8 / CPL;
     const int lane = lane_id();
@@ -879,13 +919,42 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
     const int cl = lane % LPR;
     const int h = (blockIdx.x * kRWaves + wave) * RPL + r;
 
-    // Everything this wave reads from memory is requested up front: ids and
-    // weights (lane k holds slot k), s[h], then its W2 rows of a whole batch.
+    // Everything this wave reads is requested up front, in the order it is
+    // needed: a wave's vector loads complete in issue order, so a wait for one
+    // load also waits for every load issued before it.  First ids and weights
+    // (lane k holds slot k) and s[h]; then the activations to stage (indices
+    // past the end re-read the last chunk); then, with SH, the shared down row
+    // and act_s; and after the ids are in, the W2 rows of a whole batch.
     // Batch slots past K reload the last expert's row (a cache hit, unused),
-    // so the loads need no branches and all stay ahead of the staging below.
+    // so the loads need no branches.
     const int my_id = lane < K ? ids[lane] : 0;
     const float my_tw = lane < K ? tw[lane] : 0.0f;
-    const float s_h = s_in ? s_in[h] : 0.0f;
+    const float s_h = !SH && s_in ? s_in[h] : 0.0f;
+    const int n4 = K * I / 4;
+    f32x4 st[STAGE];
+    {
+        const f32x4 *a4 = reinterpret_cast<const f32x4 *>(act);
+#pragma unroll
+        for (int i = 0; i < STAGE; ++i) {
+            const int q = threadIdx.x + i * kRBlock;
+            st[i] = a4[q < n4 ? q : n4 - 1];
+        }
+    }
+    f16x8 sv[CPL];
+    f32x4 sa[2 * CPL];
+    if constexpr (SH) {
+        const f16x8 *srow = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * I);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sv[c] = stream_load(srow + c * LPR + cl);
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(act_s + (c * LPR + cl) * 8);
+            sa[2 * c] = ap[0];
+            sa[2 * c + 1] = ap[1];
+        }
+        // the shared row goes out before the wait for the ids
+        __builtin_amdgcn_sched_barrier(0);
+    }
     f16x8 wv[BATCH][CPL];
     auto load_batch = [&](int u0) {
 #pragma unroll
@@ -898,21 +967,14 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
         }
     };
     load_batch(0);
-    // stage act: a thread's loads all in flight before it writes LDS (indices
-    // past the end re-read the last chunk instead of branching)
-    const int n4 = K * I / 4;
+    // Stage act.  The store is unconditional (past the end, the last chunk
+    // stores its own value again): a store under a branch would pull its
+    // load into the branch, behind the W2 batch.
     f32x4 *l4 = reinterpret_cast<f32x4 *>(lds);
-    const f32x4 *a4 = reinterpret_cast<const f32x4 *>(act);
-    f32x4 st[STAGE];
 #pragma unroll
     for (int i = 0; i < STAGE; ++i) {
         const int q = threadIdx.x + i * kRBlock;
-        st[i] = a4[q < n4 ? q : n4 - 1];
-    }
-#pragma unroll
-    for (int i = 0; i < STAGE; ++i) {
-        const int q = threadIdx.x + i * kRBlock;
-        if (q < n4) l4[q] = st[i];
+        l4[q < n4 ? q : n4 - 1] = st[i];
     }
     __syncthreads();
 
@@ -948,8 +1010,15 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
                 if (t < K - u0) acc = fmaf(weight(u0 + t), slot_dot(t, u0 + t), acc);
         }
     }
+    float s_add = s_h;
+    if constexpr (SH) {
+        float d = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) d = dot8_f32(sv[c], sa[2 * c], sa[2 * c + 1], d);
+        s_add = group_sum<LPR>(fmaf(1.0f, d, 0.0f));
+    }
     const float t = group_sum<LPR>(acc);
-    if (lane == group_holder<LPR>(r)) y[h] = (f16)(s_in ? t + s_h : t);
+    if (lane == group_holder<LPR>(r)) y[h] = (f16)(SH || s_in ? t + s_add : t);
 }
 
 // ---------------------------------------------------------------- grouping
@@ -1433,32 +1502,46 @@ bool lean_ok(int M, int H, int E, int I, int K, int Is)
            (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
 }
 
-template <int HC, int NPL, int LPR, int CPL>
-static void launch_expand_t(dim3 grid, const void *x, const void *w13, const void *wsd,
-                            const float *logits, const float *act_s, int E, int I, int K, int Is,
+// Where a layer's shared-expert work goes (the three-launch path): with
+// Is == I the shared down projection shares the routed one's lane mapping,
+// so its gate/up rows stream in k_expand and its down rows in k_reduce;
+// otherwise gate/up beside the router and down in k_expand.
+static inline bool shared_folded(int I, int Is) { return Is == I; }
+
+template <int HC, int NPL, int LPR, int CPL, int SM>
+static void launch_expand_t(dim3 grid, const void *x, const void *w13, const void *wsh,
+                            const float *logits, float *act_s, int E, int I, int K, int Is,
                             int renorm, int32_t *ids, float *w, float *act, float *s_out,
                             hipStream_t s)
 {
-    hipLaunchKernelGGL((k_expand<HC, NPL, LPR, CPL>), grid, dim3(kBlock), 0, s, (const f16 *)x,
-                       (const f16 *)w13, (const f16 *)wsd, logits, act_s, E, I, K, Is, renorm,
-                       ids, w, act, s_out);
+    hipLaunchKernelGGL((k_expand<HC, NPL, LPR, CPL, SM>), grid, dim3(kBlock), 0, s,
+                       (const f16 *)x, (const f16 *)w13, (const f16 *)wsh, logits, act_s, E, I,
+                       K, Is, renorm, ids, w, act, s_out);
 }
 
 template <int HC, int NPL>
-static void launch_expand_n(dim3 grid, const void *x, const void *w13, const void *wsd,
-                            const float *logits, const float *act_s, int E, int I, int K, int Is,
-                            int renorm, int32_t *ids, float *w, float *act, float *s_out,
-                            hipStream_t s)
+static void launch_expand_n(dim3 grid, const void *x, const void *w13, const void *wsgu,
+                            const void *wsd, const float *logits, float *act_s, int E, int I,
+                            int K, int Is, int renorm, int32_t *ids, float *w, float *act,
+                            float *s_out, hipStream_t s)
 {
+    if (Is == 0) {
+        launch_expand_t<HC, NPL, 64, 1, kExpandNoShared>(grid, x, w13, nullptr, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+        return;
+    }
+    if (shared_folded(I, Is)) {
+        launch_expand_t<HC, NPL, 64, 1, kExpandSharedGateUp>(grid, x, w13, wsgu, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+        return;
+    }
     // the shared down projection's lane mapping (rows of length Is)
+    constexpr int D = kExpandSharedDown;
     switch (Is) {
-    case 0:
-    case 512: launch_expand_t<HC, NPL, 64, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    case 64: launch_expand_t<HC, NPL, 8, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    case 128: launch_expand_t<HC, NPL, 16, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    case 256: launch_expand_t<HC, NPL, 32, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    case 1024: launch_expand_t<HC, NPL, 64, 2>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    default: launch_expand_t<HC, NPL, 64, 4>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 512: launch_expand_t<HC, NPL, 64, 1, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 64: launch_expand_t<HC, NPL, 8, 1, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 128: launch_expand_t<HC, NPL, 16, 1, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 256: launch_expand_t<HC, NPL, 32, 1, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    case 1024: launch_expand_t<HC, NPL, 64, 2, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
+    default: launch_expand_t<HC, NPL, 64, 4, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
     }
 }
 
@@ -1468,46 +1551,69 @@ static hipError_t launch_lean_hc(const void *x, const void *wr, const void *w13,
                                  int32_t *ids, float *w, float *logits, float *act, float *act_s,
                                  float *s_out, int stage, hipStream_t s)
 {
-    const int rb = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+    constexpr int H = 512 * HC;
+    const bool router_only = Is == 0 || shared_folded(I, Is);
     if (stage == 0 || stage == 1) {
-        hipLaunchKernelGGL((k_router_shared<HC>), dim3(rb + Is / kWavesPerBlock), dim3(kBlock), 0,
-                           s, (const f16 *)x, (const f16 *)wr, (const f16 *)wsgu, E, Is, logits,
-                           act_s);
+        if (router_only) {
+            hipLaunchKernelGGL((k_router1<HC>), dim3(E), dim3(kWave), 0, s, (const f16 *)x,
+                               (const f16 *)wr, logits);
+        } else {
+            const int rb = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+            hipLaunchKernelGGL((k_router_shared<HC>), dim3(rb + Is / kWavesPerBlock),
+                               dim3(kBlock), 0, s, (const f16 *)x, (const f16 *)wr,
+                               (const f16 *)wsgu, E, Is, logits, act_s);
+        }
         const hipError_t err = last();
         if (err != hipSuccess || stage == 1) return err;
     }
     if (stage != 0 && stage != 2) return hipSuccess;
-    constexpr int H = 512 * HC;
-    const int shared_blocks = Is ? H / (kWavesPerBlock * (kWave / lpr_of(Is))) : 0;
+    const int shared_blocks = Is == 0 ? 0
+                              : shared_folded(I, Is) ? Is / kWavesPerBlock
+                                                     : H / (kWavesPerBlock * (kWave / lpr_of(Is)));
     const dim3 grid(K * (I / kWavesPerBlock) + shared_blocks);
     if (E <= kWave)
-        launch_expand_n<HC, 1>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+        launch_expand_n<HC, 1>(grid, x, w13, wsgu, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
     else if (E <= 4 * kWave)
-        launch_expand_n<HC, 4>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+        launch_expand_n<HC, 4>(grid, x, w13, wsgu, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
     else
-        launch_expand_n<HC, kMaxExperts / kWave>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+        launch_expand_n<HC, kMaxExperts / kWave>(grid, x, w13, wsgu, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
     return last();
 }
 
+template <int LPR, int CPL, bool SH>
+static void launch_reduce_s(dim3 grid, size_t lds, int stage, const float *act, const f16 *w2,
+                            const int32_t *ids, const float *w, const float *s_in, const f16 *wsd,
+                            const float *act_s, int H, int I, int K, f16 *y, hipStream_t s)
+{
+    const dim3 block(kRBlock);
+    if (stage <= 1)
+        hipLaunchKernelGGL((k_reduce<LPR, CPL, 1, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+    else if (stage <= 2)
+        hipLaunchKernelGGL((k_reduce<LPR, CPL, 2, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+    else if (stage <= 4)
+        hipLaunchKernelGGL((k_reduce<LPR, CPL, 4, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+    else
+        hipLaunchKernelGGL((k_reduce<LPR, CPL, 8, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+}
+
+// shared: the shared down projection runs here (wsd, act_s), else s_in (or
+// nullptr without a shared expert) is added
 template <int LPR, int CPL>
 static hipError_t launch_reduce_t(const float *act, const void *w2, const int32_t *ids,
-                                  const float *w, const float *s_in, int H, int I, int K,
-                                  void *y, hipStream_t s)
+                                  const float *w, const float *s_in, const void *wsd,
+                                  const float *act_s, bool shared, int H, int I, int K, void *y,
+                                  hipStream_t s)
 {
     constexpr int rows = kRWaves * (kWave / LPR);
     const size_t lds = (size_t)K * I * sizeof(float);
     const int stage = (K * I / 4 + kRBlock - 1) / kRBlock;
-    const dim3 grid(H / rows), block(kRBlock);
-    const f16 *w2h = (const f16 *)w2;
-    f16 *yh = (f16 *)y;
-    if (stage <= 1)
-        hipLaunchKernelGGL((k_reduce<LPR, CPL, 1>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
-    else if (stage <= 2)
-        hipLaunchKernelGGL((k_reduce<LPR, CPL, 2>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
-    else if (stage <= 4)
-        hipLaunchKernelGGL((k_reduce<LPR, CPL, 4>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
+    const dim3 grid(H / rows);
+    if (shared)
+        launch_reduce_s<LPR, CPL, true>(grid, lds, stage, act, (const f16 *)w2, ids, w, nullptr,
+                                        (const f16 *)wsd, act_s, H, I, K, (f16 *)y, s);
     else
-        hipLaunchKernelGGL((k_reduce<LPR, CPL, 8>), grid, block, lds, s, act, w2h, ids, w, s_in, H, I, K, yh);
+        launch_reduce_s<LPR, CPL, false>(grid, lds, stage, act, (const f16 *)w2, ids, w, s_in,
+                                         nullptr, nullptr, H, I, K, (f16 *)y, s);
     return last();
 }
 
@@ -1621,14 +1727,15 @@ hipError_t launch_lean(const void *x, const void *wr, const void *w13, const voi
         }
         if (err != hipSuccess || stage != 0) return err;
     }
-    const float *s_in = Is ? s_out : nullptr;
+    const bool folded = Is != 0 && shared_folded(I, Is);
+    const float *s_in = Is && !folded ? s_out : nullptr;
     switch (I) {
-    case 64: return launch_reduce_t<8, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
-    case 128: return launch_reduce_t<16, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
-    case 256: return launch_reduce_t<32, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
-    case 512: return launch_reduce_t<64, 1>(act, w2, ids, w, s_in, H, I, K, y, s);
-    case 1024: return launch_reduce_t<64, 2>(act, w2, ids, w, s_in, H, I, K, y, s);
-    case 2048: return launch_reduce_t<64, 4>(act, w2, ids, w, s_in, H, I, K, y, s);
+    case 64: return launch_reduce_t<8, 1>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
+    case 128: return launch_reduce_t<16, 1>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
+    case 256: return launch_reduce_t<32, 1>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
+    case 512: return launch_reduce_t<64, 1>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
+    case 1024: return launch_reduce_t<64, 2>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
+    case 2048: return launch_reduce_t<64, 4>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
     }
     return hipErrorInvalidValue;
 }
