@@ -41,7 +41,7 @@ METRIC = "MoE decode µs/layer and achieved HBM GB/s (% of MI355X peak), M=1"
 HBM_PEAK_GBS = 8000.0
 LAYERS = 36
 COUNTERS = os.path.join(ROOT, "profiles", "k_expand_counters_full_e256_k8_i512.json")
-STAGES = ("k_router_shared", "k_expand", "k_reduce")
+STAGES = ("k_router1", "k_expand", "k_reduce")
 KERNEL_SRC = os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", "moe_kernels.hip")
 PF_METRIC = "MoE prefill tokens/s through one full-width layer (T tokens per layer)"
 PF_STAGES = ("k_pf_router", "k_pf_topk", "k_pf_plan", "k_pf_w13", "k_pf_w2", "k_pf_combine")
@@ -68,12 +68,15 @@ def layer_bytes(sh, n_distinct):
 
 def stage_bytes(sh):
     """Algorithmic bytes of each of the three launches of one layer at M=1 (K
-    distinct experts): weights read once, x once, and the small tensors each
-    kernel reads or writes (logits, activations, s, ids/weights, y)."""
+    distinct experts) with a shared expert as wide as a routed one, or none
+    (the benched shapes): the router alone; the routed and shared gate/up rows;
+    the routed and shared down rows.  Weights read once, x once, and the small
+    tensors each kernel reads or writes (logits, activations, ids/weights, y)."""
     H, E, K, I, Is = sh.H, sh.E, sh.K, sh.I, sh.Is
-    router = 2 * E * H + 2 * 2 * Is * H + 2 * H + 4 * E + 4 * Is
-    expand = 2 * K * 2 * I * H + 2 * H * Is + 2 * H + 4 * E + 4 * Is + 4 * K * I + 4 * H + 8 * K
-    reduce = 2 * K * H * I + 4 * K * I + 8 * K + 4 * H + 2 * H
+    assert Is in (0, I), "stage bytes are for the folded shared-expert placement"
+    router = 2 * E * H + 2 * H + 4 * E
+    expand = 2 * K * 2 * I * H + 2 * 2 * Is * H + 2 * H + 4 * E + 4 * K * I + 4 * Is + 8 * K
+    reduce = 2 * K * H * I + 2 * H * Is + 4 * K * I + 4 * Is + 8 * K + 2 * H
     return dict(zip(STAGES, (router, expand, reduce)))
 
 
@@ -421,7 +424,7 @@ def summarize_counters(fetch_dir, write_dir, out_path, cmds, prefill=0):
     else:
         sh = synth.SHAPES["full_e256_k8_i512"]
         algo = stage_bytes(sh)
-        other_names = ("k_router_shared", "k_reduce")
+        other_names = ("k_router1", "k_reduce")
     others = {}
     for k in other_names:
         f, _ = per_kernel(fetch_dir, "FETCH_SIZE", k)
@@ -433,7 +436,7 @@ def summarize_counters(fetch_dir, write_dir, out_path, cmds, prefill=0):
     res = {
         "kernel": ("k_pf_w13 (grouped gate/up GEMM + SiLU*mul, routed and shared experts), T=%d"
                    % prefill) if prefill else
-                  "k_expand<4,4,64,1> (routed gate/up + SiLU*mul, shared down), M=1",
+                  "k_expand<4,4,64,1,2> (routed and shared gate/up + SiLU*mul), M=1",
         "workload": ("full-width prefill layer H=2048 E=256 K=8 I=512 Is=512, T=%d tokens"
                      % prefill) if prefill else
                     "full-width layer H=2048 E=256 K=8 I=512 Is=512, M=1, 36 layers rotating",
