@@ -476,6 +476,18 @@ def summarize_trace(trace_dir, out_path, cmd):
         short = n.split("(")[0][:90]
         lines.append("| `%s` | %d | %.3f | %.3f | %.3f |" % (short, len(d), sum(d) / len(d) / 1e3,
                                                           min(d) / 1e3, max(d) / 1e3))
+    # dispatches inside the per-kernel stage graphs that bench times (each
+    # neighbour is the same kernel), next to the average over every dispatch
+    runs = {}
+    for i in range(1, len(ours) - 1):
+        if ours[i - 1][2] == ours[i][2] == ours[i + 1][2]:
+            runs.setdefault(ours[i][2], []).append(ours[i][1] - ours[i][0])
+    if runs:
+        lines += ["", "Inside the stage graphs (dispatches whose neighbours are the same kernel):", "",
+                  "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for n, d in sorted(runs.items(), key=lambda kv: -sum(kv[1])):
+            lines.append("| `%s` | %d | %.3f | %.3f | %.3f |" % (
+                n.split("(")[0][:90], len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, max(d) / 1e3))
     if gaps:
         gaps.sort()
         lines += ["", "Gap between consecutive library kernels (end -> next start, < 20 us): "
