@@ -642,24 +642,54 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
                                rs, (uint32_t)(h * I + (c * LPR + cl) * 8) * 2, 0, 0));
         }
     };
-    load_batch(0, 0);
-
-    // routing weights [M, K], the distinct experts' token masks and slot
-    // bytes into LDS (read per expert and token by the combine)
-    __shared__ float s_tw[kMaxSlots];
-    __shared__ unsigned s_mask[kMaxSlots];
-    __shared__ uint64_t s_slot[kMaxSlots];
-    if (!SHARED)
-        for (int i = threadIdx.x; i < kMaxSlots; i += kSBlock) {
-            if (i < M * K) s_tw[i] = topk_w[i];
-            s_mask[i] = table->u_mask[i];
-            s_slot[i] = *reinterpret_cast<const uint64_t *>(table->u_slot[i]);
-        }
-    // stage act: 16-byte chunks, 4 in flight per thread per step
+    // A wave's vector loads complete in issue order, so what is staged in LDS
+    // is requested before the first W2 batch: the routing weights [M, K], the
+    // distinct experts' token masks and slot bytes (read per expert and token
+    // by the combine; entry indices past the end re-read the last entry), and
+    // the first kSReg 16-byte chunks per thread of the activations.  The LDS
+    // stores are unconditional (past the end, the last element's own value
+    // again): a store under a branch would pull its load behind the batch.
+    static_assert(kSBlock >= kMaxSlots, "one table entry per thread");
+    constexpr int kSReg = 2 * MT; // covers K*I <= 4096 in one pass
+    const int ti = (int)threadIdx.x < kMaxSlots ? (int)threadIdx.x : kMaxSlots - 1;
+    float tw_r = 0.0f;
+    unsigned mask_r = 0u;
+    uint64_t slot_r = 0u;
+    if constexpr (!SHARED) {
+        tw_r = topk_w[ti < M * K ? ti : M * K - 1];
+        mask_r = table->u_mask[ti];
+        slot_r = *reinterpret_cast<const uint64_t *>(table->u_slot[ti]);
+    }
     const int n4 = M * slots * I / 4;
     const f32x4 *a4 = reinterpret_cast<const f32x4 *>(act);
     f32x4 *l4 = reinterpret_cast<f32x4 *>(lds);
-    for (int q0 = 0; q0 < n4; q0 += 4 * kSBlock) {
+    f32x4 st0[kSReg];
+#pragma unroll
+    for (int i = 0; i < kSReg; ++i) {
+        const int q = threadIdx.x + i * kSBlock;
+        st0[i] = a4[q < n4 ? q : n4 - 1];
+    }
+    // keep the batch's loads together, after the staging loads and ahead of
+    // the LDS stores (which wait)
+    __builtin_amdgcn_sched_barrier(0);
+    load_batch(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    __shared__ float s_tw[kMaxSlots];
+    __shared__ unsigned s_mask[kMaxSlots];
+    __shared__ uint64_t s_slot[kMaxSlots];
+    if constexpr (!SHARED) {
+        s_tw[ti] = tw_r;
+        s_mask[ti] = mask_r;
+        s_slot[ti] = slot_r;
+    }
+#pragma unroll
+    for (int i = 0; i < kSReg; ++i) {
+        const int q = threadIdx.x + i * kSBlock;
+        l4[q < n4 ? q : n4 - 1] = st0[i];
+    }
+    // the rest of act (K*I > 4096): 16-byte chunks, 4 in flight per thread per step
+    for (int q0 = kSReg * kSBlock; q0 < n4; q0 += 4 * kSBlock) {
         f32x4 st[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
