@@ -138,10 +138,12 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
  * Results equal the three-call sequence shared_expert, moe_route,
  * moe_decode_fused bit for bit (routing outputs and y), whichever way it runs.
  *
- * For M = 1 (K*I <= 16384) it is three launches: the router rows together
- * with the shared expert's gate/up rows; the routed gate/up rows (each
- * workgroup selecting the experts from the logits itself) together with the
- * shared down rows; the routed down rows with the weighted combine.  For
+ * For M = 1 (K*I <= 16384) it is three launches: the router rows; the
+ * routed gate/up rows (each workgroup selecting the experts from the logits
+ * itself); the routed down rows with the weighted combine.  A shared expert as
+ * wide as a routed one (Is == I) has its gate/up rows in the second launch
+ * and its down rows in the third; any other width has its gate/up rows in the
+ * first launch and its down rows in the second.  For
  * M = 2..8 it is four: the router and shared gate/up rows; one workgroup
  * selecting every token's experts and grouping the distinct ones; their
  * gate/up rows with the shared down rows; the down rows with the combine.
@@ -166,10 +168,11 @@ int moe_layer_launches(int M, int H, int E, int I, int K, int Is);
 /* ---- test-only probes (not part of the decode path) --------------------- */
 
 /* One launch of moe_layer_decode's three-launch path (M = 1) alone, for timing
- * each kernel: stage 1 = router + shared gate/up (writes logits and the shared
- * activations to ws), 2 = expand (reads them; writes topk_ids, topk_w, the
- * routed activations and the shared output), 3 = reduce (reads those; writes
- * y).  A stage reads what the previous stage left in the same buffers, so
+ * each kernel: stage 1 = router (writes logits; with Is != I also the shared
+ * activations, to ws), 2 = expand (reads them; writes topk_ids, topk_w, the
+ * routed activations, and the shared activations (Is == I) or the shared
+ * output (Is != I)), 3 = reduce (reads those; writes y).  A stage reads what
+ * the previous stage left in the same buffers, so
  * only a full moe_layer_decode call (or stages 1, 2, 3 in order) on them makes
  * its inputs valid.  Arguments as for moe_layer_decode; MOE_ERR_SHAPE for a
  * stage outside 1..3 or sizes that do not take the three-launch path. */
