@@ -262,9 +262,10 @@ def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int =
 def moe_dbg_layer_stage(stage: int, x, w_router, w13, w2, w_gate_up=None, w_down=None,
                         K: int = 8, renormalize: bool = True, topk_ids=None, topk_w=None,
                         logits=None, y=None, ws=None, stream=None):
-    """Benchmark probe: launch `stage` (1 router + shared gate/up, 2 expand,
-    3 reduce) of moe_layer_decode's three-launch path alone, on buffers a full
-    call already filled.  Returns (y, topk_ids, topk_w, logits)."""
+    """Benchmark probe: launch `stage` (1 router, 2 expand, 3 reduce; the
+    shared expert's rows go with them as moe_layer_decode places them) of
+    moe_layer_decode's three-launch path alone, on buffers a full call already
+    filled.  Returns (y, topk_ids, topk_w, logits)."""
     out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
                             topk_w, logits, y, ws)
     st = _lib.lib().moe_dbg_layer_stage(int(stage), *args, _stream(stream, x.device))
