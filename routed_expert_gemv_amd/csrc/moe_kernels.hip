@@ -422,8 +422,10 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
             wu[buf][c] = stream_load(urow + c * kWave + lane);
         }
     };
-    load_pair(0, 0);
-
+    // x is requested before the first row pair and stored to LDS
+    // unconditionally (past the end, the last chunk's own value again): a
+    // wave's vector loads complete in issue order, so staging requested after
+    // the pair, or stored under a branch, would wait for the whole pair.
     constexpr int kPer = (MT * HC * kWave + kBlock - 1) / kBlock; // 16-byte chunks per thread
     const int n16 = M * HC * kWave;
     const f16x8 *x16 = reinterpret_cast<const f16x8 *>(x);
@@ -433,10 +435,13 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
         const int q = threadIdx.x + i * kBlock;
         st[i] = x16[q < n16 ? q : n16 - 1];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    load_pair(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int q = threadIdx.x + i * kBlock;
-        if (q < n16) xs[q] = st[i];
+        xs[q < n16 ? q : n16 - 1] = st[i];
     }
     __syncthreads();
 
