@@ -455,7 +455,7 @@ k_pf_w13(const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__re
     constexpr int MT = kBM / 16;
     constexpr int SL = stage_loads<kGemmWaves, MT>();
     __shared__ f16 lds[2 * kBM * kLdsRow];
-    __shared__ int rid[kBM];
+    __shared__ int rid[64 * kGemmWaves > kBM ? 64 * kGemmWaves : kBM]; // rows kBM.. unread
     TileDesc d;
     if (!read_desc(desc, d)) return;
     const int t = threadIdx.x, lane = t & 63;
@@ -466,9 +466,15 @@ k_pf_w13(const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__re
     const bool active = j0 < Ig;
     const int j = min(j0 + (lane & 15), Ig - 1);
     const f16 *brow[2] = {wbase + (size_t)j * H, wbase + (size_t)(Ig + j) * H};
+    // The tile's pair-list entry is requested before the first weight step
+    // and stored unconditionally (threads past the tile's rows store into the
+    // unread tail of rid): a wave's vector loads complete in issue order, so
+    // an entry requested after the weights, or stored under a branch, would
+    // wait for them, and the token rows could not be requested until then.
+    const int pv = perm[d.first + min(t, max(d.rows - 1, 0))];
     f16x8 bb[kDepth + 1][2][2];
     load_b<2>(brow, 0, lane >> 4, bb[0]);
-    if (t < kBM) rid[t] = t < d.rows ? (shared ? d.first + t : perm[d.first + t]) : -1;
+    rid[t] = t < d.rows ? (shared ? d.first + t : pv) : -1;
     __syncthreads();
     const uint32_t x_bytes = (uint32_t)T * H * 2;
     TokRows<SL> arows = tok_rows<SL>(x, x_bytes);
@@ -507,7 +513,7 @@ k_pf_w2(const f16 *__restrict__ act, const f16 *__restrict__ act_s, const f16 *_
     constexpr int MT = kBM / 16;
     constexpr int SL = stage_loads<kGemmWaves, MT>();
     __shared__ f16 lds[2 * kBM * kLdsRow];
-    __shared__ int rid[kBM];
+    __shared__ int rid[64 * kGemmWaves > kBM ? 64 * kGemmWaves : kBM]; // rows kBM.. unread
     TileDesc d;
     if (!read_desc(desc, d)) return;
     const int t = threadIdx.x, lane = t & 63;
@@ -518,9 +524,11 @@ k_pf_w2(const f16 *__restrict__ act, const f16 *__restrict__ act_s, const f16 *_
     const bool active = c0 < H;
     const f16 *brow[2] = {wbase + (size_t)min(c0 + (lane & 15), H - 1) * kdim,
                           wbase + (size_t)min(c0 + 16 + (lane & 15), H - 1) * kdim};
+    // the pair-list entry before the first weight step, as in k_pf_w13
+    const int pv = perm[d.first + min(t, max(d.rows - 1, 0))];
     f16x8 bb[kDepth + 1][2][2];
     load_b<2>(brow, 0, lane >> 4, bb[0]);
-    if (t < kBM) rid[t] = t < d.rows ? (shared ? d.first + t : perm[d.first + t]) : -1;
+    rid[t] = t < d.rows ? (shared ? d.first + t : pv) : -1;
     __syncthreads();
     const uint32_t a_bytes = shared ? (uint32_t)T * Is * 2 : (uint32_t)T * K * I * 2;
     TokRows<SL> arows = tok_rows<SL>(shared ? act_s : act, a_bytes);
