@@ -101,3 +101,27 @@ def test_fused_stack_graph_replays_match_eager():
         if rep % 3 == 0:
             st.forward_eager()  # eager work between replays
             torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape", [
+    synth.SHAPES["full_e256_k8_i512"],                         # shared as wide as a routed expert
+    synth.LayerShape(M=1, H=2048, E=64, K=8, I=512, Is=0),     # no shared expert
+    synth.LayerShape(M=1, H=2048, E=64, K=8, I=512, Is=128),   # narrower shared expert
+], ids=_id)
+def test_layer_stages_in_order_equal_the_full_call(shape):
+    """The three launches run one at a time through moe_dbg_layer_stage (how
+    bench times each kernel) give the full call's outputs bit for bit."""
+    print("stages vs full call", shape, flush=True)
+    t = cases.draw_case(shape, 5, DEV)
+    full = DecodeLayer(t, shape)
+    full.forward()
+    staged = DecodeLayer(t, shape)
+    for stage in (1, 2, 3):
+        moe.moe_dbg_layer_stage(stage, t["x"], t["wr"], t["w13"], t["w2"], t["wsgu"], t["wsd"],
+                                shape.K, shape.renormalize, staged.topk_ids, staged.topk_w,
+                                staged.logits, staged.y, staged.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(full.logits, staged.logits)
+    assert torch.equal(full.topk_ids, staged.topk_ids)
+    assert torch.equal(full.topk_w, staged.topk_w)
+    assert torch.equal(full.y, staged.y)
