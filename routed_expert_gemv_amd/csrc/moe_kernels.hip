@@ -920,8 +920,9 @@ __global__ __launch_bounds__(kBlock) void k_expand(
 // Routed down projections and the combine, kRWaves waves per workgroup (one
 // workgroup per CU at the full-width shape).  Each wave owns RPL = 64/LPR rows
 // h, LPR lanes per row with CPL 16-byte chunks each (I = 8*LPR*CPL).  The wave
-// first issues its W2 rows for up to 8/CPL experts, then the workgroup stages
-// the activations [K*I] in LDS, then every lane accumulates as the W2 kernel
+// requests the ids and weights and its share of the activations [K*I], then
+// its W2 rows for up to 8/CPL experts; the workgroup stages the activations in
+// LDS while the rows arrive, then every lane accumulates as the W2 kernel
 // does: acc += w[k] * (its part of row h of W2[e_k] . act_k), experts in
 // routing order; one group reduction; y = fp16(acc + s[h]).
 // SH: the shared down projection is computed here too (Is == I, so its rows
