@@ -144,9 +144,11 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
  * wide as a routed one (Is == I) has its gate/up rows in the second launch
  * and its down rows in the third; any other width has its gate/up rows in the
  * first launch and its down rows in the second.  For
- * M = 2..8 it is four: the router and shared gate/up rows; one workgroup
- * selecting every token's experts and grouping the distinct ones; their
- * gate/up rows with the shared down rows; the down rows with the combine.
+ * M = 2..8: the router and shared gate/up rows; the distinct experts' gate/up
+ * rows with the shared down rows; the down rows with the combine -- three
+ * launches for M <= 4, where each workgroup of the second launch selects
+ * every token's experts and groups the distinct ones itself, four for
+ * M = 5..8, where one workgroup does that in a launch of its own.
  * Other sizes run the three calls' kernels in sequence.  See
  * moe_layer_launches.
  *   x, w_router, w13, w2  as for moe_route / moe_decode_fused
@@ -161,8 +163,8 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
                             int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
                             float *logits, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
 
-/* Number of kernels moe_layer_decode enqueues for these sizes (3 at M = 1,
- * 4 at M = 2..8), 0 for unsupported sizes or M = 0. */
+/* Number of kernels moe_layer_decode enqueues for these sizes (3 at M = 1..4,
+ * 4 at M = 5..8), 0 for unsupported sizes or M = 0. */
 int moe_layer_launches(int M, int H, int E, int I, int K, int Is);
 
 /* ---- test-only probes (not part of the decode path) --------------------- */

@@ -199,7 +199,9 @@ int moe_layer_launches(int M, int H, int E, int I, int K, int Is)
     if (!m_ok(M, H) || !h_ok(H) || !ek_ok(E, K) || !i_ok(I) || (Is != 0 && !i_ok(Is))) return 0;
     if (M == 0) return 0;
     if (lean_ok(M, H, E, I, K, Is)) return 3;
-    if (lean_m_ok(M, H, E, I, K, Is)) return 4;
+    // M <= 4: router, expand with the selection folded in, W2; else a
+    // separate selection launch before the expand
+    if (lean_m_ok(M, H, E, I, K, Is)) return mt_of(M) <= 4 ? 3 : 4;
     // shared_expert (2) + moe_route (2) + moe_decode_fused (2)
     return (Is ? 2 : 0) + 2 + 2;
 }

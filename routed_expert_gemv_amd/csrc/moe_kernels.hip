@@ -1225,6 +1225,84 @@ __global__ __launch_bounds__(kBlock) void k_expand_m(const f16 *__restrict__ x,
     }
 }
 
+// k_expand_m with the selection folded in (M <= 4, one wave per token): every
+// routed workgroup selects each token's experts (the top-k kernel's
+// arithmetic) and builds the group table in LDS itself, so the separate
+// selection launch and its hand-off are gone; workgroup 0 also writes ids,
+// weights and the table that the W2 kernel reads.  The shared workgroups are
+// k_expand_m's.  (At M = 8 each wave would select for two tokens in turn, and
+// the selection launch is kept.)
+template <int HC, int MT, int LPR, int CPL, int NPL>
+__global__ __launch_bounds__(kBlock) void k_expand_sel_m(
+    const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsd,
+    const float *__restrict__ act_s, const float *__restrict__ logits, int M, int H, int E, int I,
+    int K, int Is, int renormalize, int routed_blocks, int32_t *__restrict__ ids,
+    float *__restrict__ weights, float *__restrict__ act, float *__restrict__ s_out,
+    GroupTable *__restrict__ table)
+{
+    __shared__ f16x8 xs[MT * HC * kWave];
+    __shared__ GroupScratch g;
+    __shared__ GroupTable tl;
+    __shared__ int32_t sids[kMaxSlots];
+    const int b = blockIdx.x;
+    const int lane = lane_id();
+    if (b < routed_blocks) {
+        const int wave = threadIdx.x / kWave;
+        const bool writer = b == 0;
+        for (int m = wave; m < M; m += kWavesPerBlock) {
+            const float *L = logits + (size_t)m * E;
+            float v[NPL];
+#pragma unroll
+            for (int i = 0; i < NPL; ++i) v[i] = i * kWave + lane < E ? L[i * kWave + lane] : 0.0f;
+            int my_id;
+            float my_l;
+            const float lmax = wave_topk_vals<NPL>(v, E, K, my_id, my_l);
+            if (lane < K) sids[m * K + lane] = my_id;
+            if (writer) {
+                const float w = topk_weight_vals<NPL>(v, E, K, renormalize, my_l, lmax);
+                if (lane < K) {
+                    ids[(size_t)m * K + lane] = my_id;
+                    weights[(size_t)m * K + lane] = w;
+                }
+            }
+        }
+        __syncthreads();
+        build_group_table(sids, M, K, E, &tl, g);
+        __syncthreads();
+        if (writer) {
+            const int *src = reinterpret_cast<const int *>(&tl);
+            int *dst = reinterpret_cast<int *>(table);
+            for (int i = threadIdx.x; i < (int)(sizeof(GroupTable) / sizeof(int)); i += kBlock)
+                dst[i] = src[i];
+        }
+        w13_multi_block<HC, MT, false>(x, w13, M, I, K, act, &tl, b, xs);
+        return;
+    }
+    constexpr int RPL = kWave / LPR;
+    const int r = lane / LPR;
+    const int cl = lane % LPR;
+    const int h = ((b - routed_blocks) * kWavesPerBlock + threadIdx.x / kWave) * RPL + r;
+    const f16x8 *row = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * Is);
+    f16x8 wv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) wv[c] = stream_load(row + c * LPR + cl);
+    const bool holder = lane == group_holder<LPR>(r);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float d = 0.0f;
+        if (m < M) {
+            const float *am = act_s + (size_t)m * Is;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const f32x4 *ap = reinterpret_cast<const f32x4 *>(am + (c * LPR + cl) * 8);
+                d = dot8_f32(wv[c], ap[0], ap[1], d);
+            }
+        }
+        const float t = group_sum<LPR>(fmaf(1.0f, d, 0.0f));
+        if (m < M && holder) s_out[(size_t)m * H + h] = t;
+    }
+}
+
 // ---------------------------------------------------------------- probes
 // empty kernel (launch latency and graph node gap)
 __global__ void k_probe_empty() {}
@@ -1688,6 +1766,36 @@ static hipError_t launch_lean_m_t(const void *x, const void *wr, const void *w13
                        act_s);
     hipError_t err = last();
     if (err != hipSuccess) return err;
+    if constexpr (MT <= kWavesPerBlock) {
+        // the selection folded into the expand launch (one wave per token)
+        const int n_slots = M * K < E ? M * K : E;
+        constexpr int H = 512 * HC;
+        const int routed = n_slots * (I / (rows_per_wave_m<false>() * kWavesPerBlock));
+        const int shared = Is ? H / (kWavesPerBlock * (kWave / lpr_of(Is))) : 0;
+        const dim3 grid(routed + shared);
+#define SEL_LAUNCH(LPR_, CPL_, NPL_)                                                              \
+    hipLaunchKernelGGL((k_expand_sel_m<HC, MT, LPR_, CPL_, NPL_>), grid, dim3(kBlock), 0, s,      \
+                       (const f16 *)x, (const f16 *)w13, (const f16 *)wsd, act_s, logits, M, H, E, \
+                       I, K, Is, renorm, routed, ids, w, act, s_out, table)
+#define SEL_NPL(LPR_, CPL_)                                                                       \
+    do {                                                                                          \
+        if (E <= kWave) SEL_LAUNCH(LPR_, CPL_, 1);                                                \
+        else if (E <= 4 * kWave) SEL_LAUNCH(LPR_, CPL_, 4);                                       \
+        else SEL_LAUNCH(LPR_, CPL_, kMaxExperts / kWave);                                         \
+    } while (0)
+        switch (Is) {
+        case 0:
+        case 512: SEL_NPL(64, 1); break;
+        case 64: SEL_NPL(8, 1); break;
+        case 128: SEL_NPL(16, 1); break;
+        case 256: SEL_NPL(32, 1); break;
+        case 1024: SEL_NPL(64, 2); break;
+        default: SEL_NPL(64, 4); break;
+        }
+#undef SEL_NPL
+#undef SEL_LAUNCH
+        return last();
+    }
     if (E <= kWave)
         hipLaunchKernelGGL(k_select_m<1>, dim3(1), dim3(kSelBlock), 0, s, logits, M, E, K, renorm,
                            ids, w, table);

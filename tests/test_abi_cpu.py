@@ -180,7 +180,10 @@ def test_layer_launch_counts():
     L = _lib.lib()
     assert L.moe_layer_launches(1, 2048, 256, 512, 8, 512) == 3    # M = 1: three launches
     assert L.moe_layer_launches(1, 2048, 256, 512, 8, 0) == 3
-    assert L.moe_layer_launches(2, 2048, 256, 512, 8, 512) == 4    # several tokens
+    assert L.moe_layer_launches(2, 2048, 256, 512, 8, 512) == 3    # up to 4 tokens: selection folded
+    assert L.moe_layer_launches(4, 2048, 256, 512, 8, 512) == 3
+    assert L.moe_layer_launches(5, 2048, 256, 512, 8, 512) == 4    # 5..8 tokens: a selection launch
+    assert L.moe_layer_launches(8, 2048, 256, 512, 8, 512) == 4
     assert L.moe_layer_launches(1, 2048, 16, 2048, 16, 0) == 4     # K*I above the LDS stage
     assert L.moe_layer_launches(0, 2048, 256, 512, 8, 512) == 0
     assert L.moe_layer_launches(9, 2048, 256, 512, 8, 512) == 0
