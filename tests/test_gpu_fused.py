@@ -126,3 +126,32 @@ def test_layer_stages_in_order_equal_the_full_call(shape):
     assert torch.equal(full.topk_ids, staged.topk_ids)
     assert torch.equal(full.topk_w, staged.topk_w)
     assert torch.equal(full.y, staged.y)
+
+
+@pytest.mark.parametrize("name", ["batch2_e256_k8_i512", "batch8_e256_k8_i512"])
+def test_small_batch_stack_graph_replays_match_eager(name):
+    """Small-batch layers (the selection folded into the expand launch at
+    M <= 4, a launch of its own at M = 8) under hipGraph replay: every replay
+    equals the eager results bit for bit, with eager work between replays."""
+    sh = synth.SHAPES[name]
+    print("small-batch stack graph", name, flush=True)
+    layers = [DecodeLayer(synth.draw_layer(sh, s, DEV), sh) for s in range(4)]
+    for l in layers:
+        l.forward()
+    torch.cuda.synchronize()
+    eager = [(l.y.clone(), l.topk_ids.clone(), l.topk_w.clone()) for l in layers]
+    st = DecodeStack(layers)
+    st.capture()
+    for rep in range(6):
+        for l in layers:
+            l.y.zero_()
+            l.topk_ids.zero_()
+        st.replay()
+        torch.cuda.synchronize()
+        for i, l in enumerate(layers):
+            assert torch.equal(l.y, eager[i][0]), "replay %d layer %d" % (rep, i)
+            assert torch.equal(l.topk_ids, eager[i][1])
+            assert torch.equal(l.topk_w, eager[i][2])
+        if rep % 2 == 0:
+            st.forward_eager()
+            torch.cuda.synchronize()
