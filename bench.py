@@ -472,8 +472,11 @@ def summarize_trace(trace_dir, out_path, cmd):
     lines = ["# rocprofv3 kernel trace: " + os.path.basename(out_path), "",
              "Command: `%s`" % cmd, "",
              "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+    def short_name(n):
+        return n.replace("(anonymous namespace)::", "").split("(")[0][:90]
+
     for n, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        short = n.split("(")[0][:90]
+        short = short_name(n)
         lines.append("| `%s` | %d | %.3f | %.3f | %.3f |" % (short, len(d), sum(d) / len(d) / 1e3,
                                                           min(d) / 1e3, max(d) / 1e3))
     # dispatches inside the per-kernel stage graphs that bench times (each
@@ -487,7 +490,7 @@ def summarize_trace(trace_dir, out_path, cmd):
                   "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
         for n, d in sorted(runs.items(), key=lambda kv: -sum(kv[1])):
             lines.append("| `%s` | %d | %.3f | %.3f | %.3f |" % (
-                n.split("(")[0][:90], len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, max(d) / 1e3))
+                short_name(n), len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, max(d) / 1e3))
     if gaps:
         gaps.sort()
         lines += ["", "Gap between consecutive library kernels (end -> next start, < 20 us): "
