@@ -328,10 +328,25 @@ __device__ int block_exclusive_scan(int v, int *buf, int &total)
 // Descriptors of tiles tau in [0, total) for workgroups f in [0, grid): tau =
 // (f % 8) * ceil(total / 8) + f / 8, so workgroup f (which the dispatcher
 // places on XCD f % 8) takes a run of consecutive tiles of that XCD's share;
-// the tiles of one (group, column tile) are consecutive.
-__device__ void write_descs(const int *ts, int ngroups, const int *rows_of, const int *first_of,
-                            int total, int grid, int2 *desc)
+// the tiles of one (group, column tile) are consecutive.  The group of tile
+// tau (the largest g with ts[g] <= tau) comes from a table gof in LDS filled
+// group by group when total <= kGofCap (the shared expert's long run, group
+// `wide`, by every thread), else from a binary search over ts.  Every thread
+// of the workgroup must call this.
+constexpr int kGofCap = 8192;
+__device__ void write_descs(const int *ts, int ngroups, int wide, const int *rows_of,
+                            const int *first_of, int total, int grid, int2 *desc, short *gof)
 {
+    const bool table = total <= kGofCap;
+    if (table) {
+        for (int g = threadIdx.x; g < ngroups; g += kPlanThreads)
+            if (g != wide)
+                for (int tau = ts[g]; tau < ts[g + 1]; ++tau) gof[tau] = (short)g;
+        if (wide >= 0 && wide < ngroups)
+            for (int tau = ts[wide] + threadIdx.x; tau < ts[wide + 1]; tau += kPlanThreads)
+                gof[tau] = (short)wide;
+    }
+    __syncthreads();
     const int per_xcd = (total + 7) / 8;
     for (int f = threadIdx.x; f < grid; f += kPlanThreads) {
         const int slot = f / 8;
@@ -339,10 +354,14 @@ __device__ void write_descs(const int *ts, int ngroups, const int *rows_of, cons
         int2 v = make_int2(-1, 0);
         if (slot < per_xcd && tau < total) {
             int lo = 0, hi = ngroups - 1; // largest g with ts[g] <= tau
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) / 2;
-                if (ts[mid] <= tau) lo = mid;
-                else hi = mid - 1;
+            if (table) {
+                lo = gof[tau];
+            } else {
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) / 2;
+                    if (ts[mid] <= tau) lo = mid;
+                    else hi = mid - 1;
+                }
             }
             const int g = lo;
             const int n_rows = rows_of[g];
@@ -356,6 +375,7 @@ __device__ void write_descs(const int *ts, int ngroups, const int *rows_of, cons
         }
         desc[f] = v;
     }
+    __syncthreads(); // gof is reused by the next call
 }
 
 // One workgroup: counts the (token, slot) pairs of each expert, lists them
@@ -436,8 +456,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_pf_plan(const int32_t *__restr
             if ((unsigned)e[i] < (unsigned)E)
                 perm[atomicAdd(&cursor[e[i]], 1)] = base + i * kPlanThreads + t;
     }
-    write_descs(ts13, groups, cnt, first, ts13[groups], grid13, desc13);
-    write_descs(ts2, groups, cnt, first, ts2[groups], grid2, desc2);
+    __shared__ short gof[kGofCap];
+    const int wide = shared ? E : -1;
+    write_descs(ts13, groups, wide, cnt, first, ts13[groups], grid13, desc13, gof);
+    write_descs(ts2, groups, wide, cnt, first, ts2[groups], grid2, desc2, gof);
 }
 
 // ---------------------------------------------------------------- W13 + SiLU
