@@ -398,12 +398,21 @@ __global__ __launch_bounds__(kPlanThreads) void k_pf_plan(const int32_t *__restr
     __shared__ int ts13[kMaxExperts + 2];
     __shared__ int ts2[kMaxExperts + 2];
     __shared__ int buf[kPlanThreads / 64];
+    // the pair list, when one pass covers every pair: scattered here and
+    // written out in order (scattered 4-byte global stores from one workgroup
+    // cost several times more)
+    __shared__ int sperm[kPlanThreads * kPlanIds];
     const int t = threadIdx.x;
     const int pairs = T * K;
+    const bool one_pass = pairs <= kPlanThreads * kPlanIds;
     for (int e = t; e < E; e += kPlanThreads) cnt[e] = 0;
     __syncthreads();
     // ids are read kPlanIds per thread at a time, all loads issued before the
-    // LDS atomics that use them
+    // LDS atomics that use them; with one pass they stay in registers for the
+    // listing below
+    int e0[kPlanIds];
+#pragma unroll
+    for (int i = 0; i < kPlanIds; ++i) e0[i] = -1;
     for (int base = 0; base < pairs; base += kPlanThreads * kPlanIds) {
         int e[kPlanIds];
 #pragma unroll
@@ -412,8 +421,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_pf_plan(const int32_t *__restr
             e[i] = p < pairs ? ids[p] : -1;
         }
 #pragma unroll
-        for (int i = 0; i < kPlanIds; ++i)
+        for (int i = 0; i < kPlanIds; ++i) {
+            e0[i] = e[i];
             if ((unsigned)e[i] < (unsigned)E) atomicAdd(&cnt[e[i]], 1);
+        }
     }
     __syncthreads();
     const int c = t < E ? cnt[t] : 0;
@@ -444,17 +455,25 @@ __global__ __launch_bounds__(kPlanThreads) void k_pf_plan(const int32_t *__restr
         plan->pairs = n_pairs;
     }
     __syncthreads();
-    for (int base = 0; base < pairs; base += kPlanThreads * kPlanIds) {
-        int e[kPlanIds];
-#pragma unroll
-        for (int i = 0; i < kPlanIds; ++i) {
-            const int p = base + i * kPlanThreads + t;
-            e[i] = p < pairs ? ids[p] : -1;
-        }
+    if (one_pass) {
 #pragma unroll
         for (int i = 0; i < kPlanIds; ++i)
-            if ((unsigned)e[i] < (unsigned)E)
-                perm[atomicAdd(&cursor[e[i]], 1)] = base + i * kPlanThreads + t;
+            if ((unsigned)e0[i] < (unsigned)E) sperm[atomicAdd(&cursor[e0[i]], 1)] = i * kPlanThreads + t;
+        __syncthreads();
+        for (int q = t; q < n_pairs; q += kPlanThreads) perm[q] = sperm[q];
+    } else {
+        for (int base = 0; base < pairs; base += kPlanThreads * kPlanIds) {
+            int e[kPlanIds];
+#pragma unroll
+            for (int i = 0; i < kPlanIds; ++i) {
+                const int p = base + i * kPlanThreads + t;
+                e[i] = p < pairs ? ids[p] : -1;
+            }
+#pragma unroll
+            for (int i = 0; i < kPlanIds; ++i)
+                if ((unsigned)e[i] < (unsigned)E)
+                    perm[atomicAdd(&cursor[e[i]], 1)] = base + i * kPlanThreads + t;
+        }
     }
     __shared__ short gof[kGofCap];
     const int wide = shared ? E : -1;
