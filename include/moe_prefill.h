@@ -66,7 +66,8 @@ moe_status moe_layer_prefill(const void *x, const void *w_router, const void *w1
                              size_t ws_bytes, hipStream_t stream);
 
 /* Test-only: one stage of moe_layer_prefill alone, for timing each kernel:
- * 1 router (both launches), 2 top-K, 3 plan, 4 gate/up, 5 down, 6 combine.
+ * 1 router (the partial logits), 2 top-K (their sum into logits, then the
+ * selection), 3 plan, 4 gate/up, 5 down, 6 combine.
  * A stage reads what the previous ones left in the same buffers; arguments as
  * for moe_layer_prefill; MOE_ERR_SHAPE for a stage outside 1..6. */
 moe_status moe_dbg_prefill_stage(int stage, const void *x, const void *w_router, const void *w13,

@@ -54,14 +54,16 @@ struct PrefillLayout {
     int grid13, grid2, router_split;
 };
 PrefillLayout prefill_layout(int T, int H, int E, int I, int K, int Is);
-// stage 0: all launches; 1..6: router (partial GEMMs + their sum), top-k, plan,
-// W13, W2, combine alone.
+// stage 0: all launches; 1..6: router (partial GEMMs), top-k (the partials
+// summed into logits, then the selection), plan, W13, W2, combine alone.
 hipError_t launch_prefill(const void *x, const void *wr, const void *w13, const void *w2,
                           const void *wsgu, const void *wsd, int T, int H, int E, int I, int K,
                           int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
                           void *ws, int stage, hipStream_t s);
 hipError_t launch_topk(const float *logits, int M, int E, int K, int renorm, int32_t *ids,
                        float *w, hipStream_t s);
+hipError_t launch_topk_sum(const float *part, int P, int M, int E, int K, int renorm,
+                           float *logits, int32_t *ids, float *w, hipStream_t s);
 
 inline int mt_of(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8; }
 

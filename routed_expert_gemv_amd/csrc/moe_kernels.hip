@@ -319,6 +319,43 @@ __global__ __launch_bounds__(kWave) void k_topk(const float *__restrict__ logits
     }
 }
 
+// The top-k kernel's work on logits that arrive as P partial sums over slices
+// of H (part[p][M*E], the many-token router's output): each logit is summed
+// p = 0, 1, ..., P-1 in that order and written to logits, then token m's
+// experts are selected and weighted exactly as k_topk does.
+template <int NPL>
+__global__ __launch_bounds__(kWave) void k_topk_sum(const float *__restrict__ part, int P, int M,
+                                                    int E, int K, int renormalize,
+                                                    float *__restrict__ logits,
+                                                    int32_t *__restrict__ ids,
+                                                    float *__restrict__ weights)
+{
+    const int m = blockIdx.x;
+    const int lane = lane_id();
+    const size_t n = (size_t)M * E;
+    float v[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+        const int e = i * kWave + lane;
+        v[i] = 0.0f;
+        if (e < E) {
+            const size_t o = (size_t)m * E + e;
+            float t = part[o];
+            for (int p = 1; p < P; ++p) t += part[(size_t)p * n + o];
+            v[i] = t;
+            logits[o] = t;
+        }
+    }
+    int my_id;
+    float my_l;
+    const float lmax = wave_topk_vals<NPL>(v, E, K, my_id, my_l);
+    const float w = topk_weight_vals<NPL>(v, E, K, renormalize, my_l, lmax);
+    if (lane < K) {
+        ids[(size_t)m * K + lane] = my_id;
+        weights[(size_t)m * K + lane] = w;
+    }
+}
+
 // Slot (top-k index) of token m in distinct-expert entry u: the entry's 8
 // slot bytes are read with one 8-byte load at a uniform address, which the
 // compiler issues as a scalar load.  (Reading the byte alone becomes a vector
@@ -1389,6 +1426,21 @@ hipError_t launch_topk(const float *logits, int M, int E, int K, int renorm, int
     else
         hipLaunchKernelGGL(k_topk<kMaxExperts / kWave>, dim3(M), dim3(kWave), 0, s, logits, E, K,
                            renorm, ids, w);
+    return last();
+}
+
+hipError_t launch_topk_sum(const float *part, int P, int M, int E, int K, int renorm,
+                           float *logits, int32_t *ids, float *w, hipStream_t s)
+{
+    if (E <= kWave)
+        hipLaunchKernelGGL(k_topk_sum<1>, dim3(M), dim3(kWave), 0, s, part, P, M, E, K, renorm,
+                           logits, ids, w);
+    else if (E <= 4 * kWave)
+        hipLaunchKernelGGL(k_topk_sum<4>, dim3(M), dim3(kWave), 0, s, part, P, M, E, K, renorm,
+                           logits, ids, w);
+    else
+        hipLaunchKernelGGL(k_topk_sum<kMaxExperts / kWave>, dim3(M), dim3(kWave), 0, s, part, P,
+                           M, E, K, renorm, logits, ids, w);
     return last();
 }
 

@@ -234,7 +234,7 @@ __device__ __forceinline__ bool read_desc(const int2 *desc, TileDesc &d)
 // columns each).  Workgroup: 4 waves, 64 tokens x 128 experts (two 16-expert
 // column tiles per wave); grid = P x ceil(T/64) x ceil(E/128).  Splitting H
 // gives the small router enough workgroups and a short k loop each; the
-// slices are summed in a fixed order by k_pf_logits.
+// slices are summed in a fixed order by the top-k launch (k_topk_sum).
 __global__ __launch_bounds__(kRouterBlock) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 k_pf_router(const f16 *__restrict__ x, const f16 *__restrict__ wr, int T, int H, int E, int kper,
             float *__restrict__ part)
@@ -279,17 +279,6 @@ k_pf_router(const f16 *__restrict__ x, const f16 *__restrict__ wr, int T, int H,
                 if (i < rows) out[(size_t)(m0 + i) * E + col] = acc[mt][ct][r];
             }
     }
-}
-
-// logits[i] = part[0][i] + part[1][i] + ... + part[P-1][i] (in that order).
-__global__ __launch_bounds__(256) void k_pf_logits(const float *__restrict__ part, int n, int P,
-                                                   float *__restrict__ logits)
-{
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    float v = part[i];
-    for (int p = 1; p < P; ++p) v += part[(size_t)p * n + i];
-    logits[i] = v;
 }
 
 // ---------------------------------------------------------------- plan
@@ -690,12 +679,11 @@ hipError_t launch_prefill(const void *x, const void *wr, const void *w13, const 
         hipLaunchKernelGGL(k_pf_router, dim3(router_tiles), dim3(kRouterBlock), 0, s,
                            (const f16 *)x, (const f16 *)wr, T, H, E, H / P, part);
         if ((err = last()) != hipSuccess) return err;
-        hipLaunchKernelGGL(k_pf_logits, dim3((T * E + 255) / 256), dim3(256), 0, s, part, T * E, P,
-                           logits);
-        if ((err = last()) != hipSuccess) return err;
     }
     if (stage == 0 || stage == 2) {
-        if ((err = launch_topk(logits, T, E, K, renorm, ids, w, s)) != hipSuccess) return err;
+        // the slices summed in a fixed order into logits, then the selection
+        if ((err = launch_topk_sum(part, P, T, E, K, renorm, logits, ids, w, s)) != hipSuccess)
+            return err;
     }
     if (stage == 0 || stage == 3) {
         hipLaunchKernelGGL(k_pf_plan, dim3(1), dim3(kPlanThreads), 0, s, ids, T, K, E,
