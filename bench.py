@@ -116,8 +116,21 @@ def counters_traffic(path=COUNTERS, src=KERNEL_SRC):
     return c.get("hbm_bytes_per_dispatch")
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform string."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(stack_tensors, sh, budget_s=12.0):
-    """The fp64 oracle, as it is, on this host's cores over a bounded sample."""
+    """The fp64 oracle, as it is, on this host: the same layers timed on one
+    core and on every core the process may use (half the budget each)."""
     import numpy as np
     import torch
     import oracle
@@ -135,22 +148,31 @@ def cpu_baseline(stack_tensors, sh, budget_s=12.0):
         w2 = t["w2"].index_select(0, idx).to("cpu", torch.float64).numpy()
         h["slices"] = (w13, w2)
         host.append(h)
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        h = host[done % len(host)]
-        oracle.moe_layer_fetch(h["x"], h["wr"], lambda ids, s=h["slices"]: s, h["wsgu"],
-                               h["wsd"], K=sh.K, renormalize=sh.renormalize, nthreads=nthreads)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+
+    def run(threads, budget):
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            h = host[done % len(host)]
+            oracle.moe_layer_fetch(h["x"], h["wr"], lambda ids, s=h["slices"]: s, h["wsgu"],
+                                   h["wsd"], K=sh.K, renormalize=sh.renormalize,
+                                   nthreads=threads)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return done, el
+
+    d1, e1 = run(1, budget_s / 2)
+    dn, en = run(nthreads, budget_s / 2)
     expert, _ = layer_bytes(sh, sh.K)
-    us = el / done * 1e6
-    return {"value": round(expert * done / el / 1e9, 4), "unit": "GB/s",
-            "us_per_layer": round(us, 1), "cores": nthreads, "kind": "oracle",
-            "sample": "%d layer evaluations cycling over 4 of the 36 layers (fp64 C oracle: "
-                      "router, top-k, 8 experts, shared expert), %.1f s wall" % (done, el)}
+    return {"value": round(expert * dn / en / 1e9, 4), "unit": "GB/s",
+            "us_per_layer": round(en / dn * 1e6, 1), "cores": nthreads, "kind": "oracle",
+            "value_1core": round(expert * d1 / e1 / 1e9, 4),
+            "us_per_layer_1core": round(e1 / d1 * 1e6, 1),
+            "cpu_model": cpu_model(),
+            "sample": "fp64 C oracle (router, top-k, 8 experts, shared expert) cycling over 4 "
+                      "of the 36 layers: %d layer evaluations on %d threads in %.1f s, %d on 1 "
+                      "thread in %.1f s" % (dn, nthreads, en, d1, e1)}
 
 
 def replay_percentiles(stack, n, layers):

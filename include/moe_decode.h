@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 #define MOE_MAX_TOKENS 8
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_EXPERTS 1024
@@ -78,13 +78,33 @@ typedef int moe_status;
 /* ABI version of the loaded library (MOE_ABI_VERSION it was built with). */
 int moe_abi_version(void);
 
+/* Identity of the sources the library was built from: the hex SHA-256 over
+ * the names and contents of its source and header files (static string,
+ * never NULL; "unversioned" for a build that did not set it).  Loaders compare
+ * it with the sources at hand to refuse an out-of-date binary. */
+const char *moe_build_id(void);
+
 /* Static English description of a status code; never NULL. */
 const char *moe_status_str(moe_status status);
 
-/* Bytes of device workspace `ws` that shared_expert and moe_decode_fused need
- * for these sizes (one buffer of this size serves both calls when they are
- * issued on the same stream).  Returns 0 for unsupported sizes. */
+/* Bytes of device workspace `ws` that shared_expert, moe_decode_fused and
+ * moe_layer_decode need for these sizes (one buffer of this size serves every
+ * call issued on the same stream).  Returns 0 for unsupported sizes.
+ *
+ * The first 8192 bytes of a workspace are a state block that the
+ * single-launch layer (moe_dbg_layer_stage stage 5) keeps between calls: one call counter
+ * per workgroup and its hand-off flags (no atomics are used; a flag is current
+ * when it holds the call count of this call).  It must be zero before the
+ * first call with a workspace -- allocate it zero-filled or call
+ * moe_workspace_init once -- and is then left to the library.  Word 1024 of the
+ * block counts the waits that ran out and computed the awaited data
+ * themselves (0 in normal operation; the results are the same either way).
+ * The other entry points use the workspace past the state block as scratch. */
 size_t moe_workspace_bytes(int M, int H, int E, int I, int K, int Is);
+
+/* Zeroes the state block of `ws` (ws_bytes >= 8192, 256-byte aligned) with a
+ * kernel on `stream`.  MOE_ERR_NULL / MOE_ERR_ALIGN / MOE_ERR_WORKSPACE. */
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Steps 1-2: router GEMV, top-K selection and routing weights.
  *   x           [M, H]  fp16   token activations
@@ -155,9 +175,10 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
  *   w_gate_up, w_down     shared expert [2Is, H] / [H, Is], or both NULL (Is ignored)
  *   topk_ids, topk_w, logits  outputs as for moe_route
  *   y          [M, H] fp16 out
- *   ws         >= moe_workspace_bytes(M, H, E, I, K, Is) bytes of device memory;
- *              scratch only (nothing is kept between calls).  Calls that share a
- *              ws must not overlap in time. */
+ *   ws         >= moe_workspace_bytes(M, H, E, I, K, Is) bytes of device memory,
+ *              256-byte aligned; its state block must be zero before the first
+ *              call (see moe_workspace_bytes).  Calls that share a ws must not
+ *              overlap in time. */
 moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13, const void *w2,
                             const void *w_gate_up, const void *w_down, int M, int H, int E, int I,
                             int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
@@ -169,15 +190,35 @@ int moe_layer_launches(int M, int H, int E, int I, int K, int Is);
 
 /* ---- test-only probes (not part of the decode path) --------------------- */
 
-/* One launch of moe_layer_decode's three-launch path (M = 1) alone, for timing
- * each kernel: stage 1 = router (writes logits; with Is != I also the shared
- * activations, to ws), 2 = expand (reads them; writes topk_ids, topk_w, the
- * routed activations, and the shared activations (Is == I) or the shared
- * output (Is != I)), 3 = reduce (reads those; writes y).  A stage reads what
- * the previous stage left in the same buffers, so
- * only a full moe_layer_decode call (or stages 1, 2, 3 in order) on them makes
- * its inputs valid.  Arguments as for moe_layer_decode; MOE_ERR_SHAPE for a
- * stage outside 1..3 or sizes that do not take the three-launch path. */
+/* moe_layer_decode at M = 1 by a chosen path, for tests and timing.
+ * Stages 1..3 run one launch of the three-launch path alone: 1 = router
+ * (writes logits; with Is != I also the shared activations, to ws), 2 = expand
+ * (reads them; writes topk_ids, topk_w, the routed activations, and the shared
+ * activations (Is == I) or the shared output (Is != I)), 3 = reduce (reads
+ * those; writes y).  A stage reads what the previous stage left in the same
+ * buffers, so only a full call (or stages 1, 2, 3 in order) on them makes its
+ * inputs valid.  Stage 4 runs the three-launch path whole.
+ *
+ * Stage 5 runs the layer as ONE launch, on a GPU with 256 CUs in 8 XCDs
+ * (MI355X), for H in {1024, 2048}, E <= 256, K <= 8, I in {64, ..., 1024},
+ * Is in {0, I} and K*I <= 4096: 256 workgroups of 16 waves, one per CU.  Each
+ * XCD computes every router logit itself and hands them over through its own
+ * L2; every workgroup selects the experts, streams one gate/up row pair per
+ * wave and requests the down rows of its output rows before the activations
+ * are known; the activations are exchanged once across the XCDs through
+ * device-coherent stores and flags, one workgroup per XCD watching the 256
+ * device-wide flags and relaying through a flag in its XCD's L2.  The
+ * workgroups wait on each other without atomics, through the workspace's
+ * state block (see moe_workspace_bytes); every wait is bounded, and a
+ * workgroup whose wait runs out computes the data itself, so a call always
+ * completes with the same results -- the three-launch path's bits.  On an
+ * MI355X it is slower than the three launches (the hand-offs cost more than
+ * the launches they remove), so moe_layer_decode does not use it.
+ * Stage 6 is stage 5 with every wait giving up at once (each workgroup
+ * computes the logits and every activation itself; slow, for testing that
+ * path).
+ * Arguments as for moe_layer_decode; MOE_ERR_SHAPE for a stage outside 1..6
+ * or sizes that do not take the chosen path. */
 moe_status moe_dbg_layer_stage(int stage, const void *x, const void *w_router, const void *w13,
                                const void *w2, const void *w_gate_up, const void *w_down, int M,
                                int H, int E, int I, int K, int Is, int renormalize,

@@ -66,6 +66,14 @@ def workspace(M: int, H: int, E: int, I: int, K: int, Is: int = 0, device=None) 
     return torch.zeros(n, dtype=torch.uint8, device=device or torch.cuda.current_device())
 
 
+def moe_workspace_init(ws, stream=None) -> None:
+    """Zero the state block at the start of a workspace (needed once before a
+    workspace that did not come from workspace() is first used)."""
+    _dev_tensor("ws", ws, torch.uint8)
+    _check("moe_workspace_init", _lib.lib().moe_workspace_init(_ptr(ws), ws.numel(),
+                                                               _stream(stream, ws.device)))
+
+
 def moe_route(x, w_router, K: int, renormalize: bool = True, topk_ids=None, topk_w=None,
               logits=None, stream=None):
     """Router GEMV + top-K + routing weights.  Returns (topk_ids, topk_w, logits)."""
@@ -106,7 +114,7 @@ def shared_expert(x, w_gate_up, w_down, s_out=None, ws=None, stream=None):
     if s_out.numel() != M * H:
         raise ValueError("s_out must have M*H elements")
     if ws is None:
-        ws = torch.empty(max(M, 1) * Is * 4, dtype=torch.uint8, device=dev)
+        ws = workspace(max(M, 1), H, 1, 64, 1, Is, dev)
     _dev_tensor("ws", ws, torch.uint8)
     st = _lib.lib().shared_expert(_ptr(x), _ptr(w_gate_up), _ptr(w_down), M, H, Is, _ptr(s_out),
                                   _ptr(ws), ws.numel(), _stream(stream, dev))
@@ -262,10 +270,13 @@ def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int =
 def moe_dbg_layer_stage(stage: int, x, w_router, w13, w2, w_gate_up=None, w_down=None,
                         K: int = 8, renormalize: bool = True, topk_ids=None, topk_w=None,
                         logits=None, y=None, ws=None, stream=None):
-    """Benchmark probe: launch `stage` (1 router, 2 expand, 3 reduce; the
-    shared expert's rows go with them as moe_layer_decode places them) of
-    moe_layer_decode's three-launch path alone, on buffers a full call already
-    filled.  Returns (y, topk_ids, topk_w, logits)."""
+    """Test and benchmark probe of moe_layer_decode at M = 1.  Stage 1, 2, 3:
+    one launch of the three-launch path (router; expand; reduce -- the shared
+    expert's rows go with them as that path places them), alone, on buffers a
+    full call already filled; 4: the three-launch path whole; 5: the
+    single-launch path; 6: the single-launch path with every wait giving up at
+    once (each workgroup computes what it would have waited for).
+    Returns (y, topk_ids, topk_w, logits)."""
     out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
                             topk_w, logits, y, ws)
     st = _lib.lib().moe_dbg_layer_stage(int(stage), *args, _stream(stream, x.device))

@@ -1,6 +1,12 @@
-"""Build libmoe_decode.so (gfx950) in-tree with hipcc."""
+"""Build libmoe_decode.so (gfx950) in-tree with hipcc.
+
+The library carries the SHA-256 of the sources it was built from (exported as
+moe_build_id); the loader refuses a library whose id differs from the
+sources in the tree, so a test never runs an old binary by accident.
+"""
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -10,10 +16,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_decode.so")
-SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_prefill.hip"),
-           os.path.join(CSRC, "moe_abi.cpp")]
-HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(INCLUDE, "moe_decode.h"),
-           os.path.join(INCLUDE, "moe_prefill.h")]
+SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_layer1.hip"),
+           os.path.join(CSRC, "moe_prefill.hip"), os.path.join(CSRC, "moe_abi.cpp")]
+HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(CSRC, "moe_device.h"),
+           os.path.join(INCLUDE, "moe_decode.h"), os.path.join(INCLUDE, "moe_prefill.h")]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for every HIP file of this library.
 HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -26,7 +32,20 @@ def hipcc() -> str:
     return p if os.path.exists(p) else "hipcc"
 
 
+def source_id() -> str:
+    """SHA-256 (hex) over the names and contents of the sources and headers."""
+    h = hashlib.sha256()
+    for path in sorted(SOURCES + HEADERS):
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+        h.update(b"\0")
+    return h.hexdigest()
+
+
 def stale() -> bool:
+    """True when LIB is missing or older than a source (mtime; the loader's
+    content check is the authoritative one)."""
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
@@ -38,7 +57,8 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if not force and not stale():
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-I" + INCLUDE, "-I" + CSRC] + SOURCES + ["-o", tmp]
+    cmd = [hipcc()] + HIPCC_FLAGS + ['-DMOE_BUILD_ID="%s"' % source_id(), "-I" + INCLUDE,
+                                     "-I" + CSRC] + SOURCES + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed (%d):\n%s\n%s" % (r.returncode, " ".join(cmd), r.stderr))

@@ -81,10 +81,20 @@ static moe_status layer_decode(const void *x, const void *w_router, const void *
         (shared && (!al(w_gate_up, 16) || !al(w_down, 16))))
         return MOE_ERR_ALIGN;
     if (ws_bytes < routed_ws_bytes(M, I, K)) return MOE_ERR_WORKSPACE;
-    if (stage != 0 && (stage < 1 || stage > 3 || !lean_ok(M, H, E, I, K, Is))) return MOE_ERR_SHAPE;
+    // stage 1..3: one launch of the three-launch path; stage 4: the three-launch
+    // path whole; 5: the single launch; 6: the single launch with every wait
+    // giving up at once
+    if (stage < 0 || stage > 6) return MOE_ERR_SHAPE;
+    if (stage >= 1 && stage <= 4 && !lean_ok(M, H, E, I, K, Is)) return MOE_ERR_SHAPE;
+    if (stage >= 5 && !layer1_ok(M, H, E, I, K, Is)) return MOE_ERR_SHAPE;
     char *base = static_cast<char *>(ws);
-    float *act_s = reinterpret_cast<float *>(base);
+    float *act_s = reinterpret_cast<float *>(base + kScratch);
     float *act = reinterpret_cast<float *>(base + kRoutedActOffset);
+    if (stage >= 5)
+        return hip_status(launch_layer1(x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is,
+                                        renormalize, topk_ids, topk_w, logits, y, ws,
+                                        stage == 6 ? 0u : kLayer1Spin, stream));
+    if (stage == 4) stage = 0;
     if (lean_ok(M, H, E, I, K, Is))
         return hip_status(launch_lean(x, w_router, w13, w2, w_gate_up, w_down, H, E, I, K, Is,
                                       renormalize, topk_ids, topk_w, logits, y, act, act_s,
@@ -107,9 +117,15 @@ static moe_status layer_decode(const void *x, const void *w_router, const void *
     return hip_status(err);
 }
 
+#ifndef MOE_BUILD_ID
+#define MOE_BUILD_ID "unversioned"
+#endif
+
 extern "C" {
 
 int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_build_id(void) { return MOE_BUILD_ID; }
 
 const char *moe_status_str(moe_status s)
 {
@@ -151,9 +167,10 @@ moe_status shared_expert(const void *x, const void *w_gate_up, const void *w_dow
     if (!x || !w_gate_up || !w_down || !s_out || !ws) return MOE_ERR_NULL;
     if (!al(x, 16) || !al(w_gate_up, 16) || !al(w_down, 16) || !al(s_out, 4) || !al(ws, 256))
         return MOE_ERR_ALIGN;
-    if (ws_bytes < (size_t)M * Is * sizeof(float)) return MOE_ERR_WORKSPACE;
+    if (ws_bytes < kScratch + (size_t)M * Is * sizeof(float)) return MOE_ERR_WORKSPACE;
     return hip_status(launch_shared(x, w_gate_up, w_down, M, H, Is, s_out,
-                                    static_cast<float *>(ws), stream));
+                                    reinterpret_cast<float *>(static_cast<char *>(ws) + kScratch),
+                                    stream));
 }
 
 moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
@@ -183,13 +200,21 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
                         topk_ids, topk_w, logits, y, ws, ws_bytes, 0, stream);
 }
 
+moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!ws) return MOE_ERR_NULL;
+    if (!al(ws, 256)) return MOE_ERR_ALIGN;
+    if (ws_bytes < kStateBytes) return MOE_ERR_WORKSPACE;
+    return hip_status(launch_state_clear(ws, stream));
+}
+
 moe_status moe_dbg_layer_stage(int stage, const void *x, const void *w_router, const void *w13,
                                const void *w2, const void *w_gate_up, const void *w_down, int M,
                                int H, int E, int I, int K, int Is, int renormalize,
                                int32_t *topk_ids, float *topk_w, float *logits, void *y, void *ws,
                                size_t ws_bytes, hipStream_t stream)
 {
-    if (stage < 1 || stage > 3) return MOE_ERR_SHAPE;
+    if (stage < 1 || stage > 6) return MOE_ERR_SHAPE;
     return layer_decode(x, w_router, w13, w2, w_gate_up, w_down, M, H, E, I, K, Is, renormalize,
                         topk_ids, topk_w, logits, y, ws, ws_bytes, stage, stream);
 }

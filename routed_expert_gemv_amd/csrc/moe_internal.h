@@ -25,14 +25,37 @@ struct GroupTable {
     signed char u_slot[kMaxSlots][kMaxTokens];
 };
 
+// State the single-launch layer keeps in the workspace between calls (zero
+// before the first call): one call counter per workgroup and the hand-off
+// flags, which hold the call count of the call that last set them.
+constexpr int kLayer1Grid = 256; // workgroups of the single-launch layer (one per CU)
+constexpr int kPerXcd = 32;      // of them on each of the 8 XCDs
+struct Layer1State {
+    unsigned epoch[kLayer1Grid];     // calls each workgroup has completed
+    unsigned flag_route[8][kPerXcd]; // router rows stored, per XCD and workgroup
+    unsigned flag_act[kLayer1Grid];  // activations published, per workgroup
+    unsigned flag_xact[8][kPerXcd];  // [x][0]: every activation published (seen by XCD x)
+    unsigned gave_up;                // waits that ran out and computed the data themselves
+    unsigned pad_[2047 - 4 * kLayer1Grid];
+};
+static_assert(sizeof(Layer1State) == 8192, "state block");
+
 // Workspace layout (bytes from the start of ws, 256-byte aligned regions):
-//   [0, kSharedActBytes)                  shared-expert activations [M, Is] fp32
+//   [0, kStateBytes)                      Layer1State (kept between calls)
+//   [kScratch, +kSharedActBytes)          shared-expert activations [M, Is] fp32
 //   [kGroupOffset, +sizeof(GroupTable))   GroupTable
 //   [kSharedOutOffset, +M*H*4)            shared-expert output [M, H] fp32
 //   [kRoutedActOffset, +M*K*I*4)          routed activations [M, K, I] fp32
+// The single-launch layer uses [kLayer1LogitsOffset, +8*E*4) for each XCD's
+// logits and [kLayer1ActOffset, +(K*I + Is)*4) for the published activations
+// (inside the scratch regions above, which it does not otherwise use).
 constexpr size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+constexpr size_t kStateBytes = sizeof(Layer1State);
+constexpr size_t kScratch = kStateBytes;
 constexpr size_t kSharedActBytes = (size_t)kMaxTokens * kMaxInter * sizeof(float);
-constexpr size_t kGroupOffset = align256(kSharedActBytes);
+constexpr size_t kLayer1LogitsOffset = kScratch;
+constexpr size_t kLayer1ActOffset = kLayer1LogitsOffset + 8 * kMaxExperts * sizeof(float);
+constexpr size_t kGroupOffset = kScratch + align256(kSharedActBytes);
 constexpr size_t kSharedOutOffset = kGroupOffset + align256(sizeof(GroupTable));
 constexpr size_t kSharedOutBytes = (size_t)kMaxTokens * 4096 * sizeof(float);
 constexpr size_t kRoutedActOffset = kSharedOutOffset + align256(kSharedOutBytes);
@@ -93,6 +116,15 @@ hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const v
                          int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
                          float *act, float *act_s, float *s_out, GroupTable *table, hipStream_t s);
 bool lean_ok(int M, int H, int E, int I, int K, int Is);
+// The layer at M = 1 in one launch (moe_layer1.hip); spin bounds each wait
+// (0: every wait gives up at once and computes the data itself).
+bool layer1_ok(int M, int H, int E, int I, int K, int Is);
+hipError_t launch_layer1(const void *x, const void *wr, const void *w13, const void *w2,
+                         const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
+                         int renorm, int32_t *ids, float *w, float *logits, void *y, void *ws,
+                         unsigned spin, hipStream_t s);
+constexpr unsigned kLayer1Spin = 1u << 16;
+hipError_t launch_state_clear(void *ws, hipStream_t s);
 hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
                        int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,

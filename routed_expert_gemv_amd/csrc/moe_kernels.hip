@@ -20,117 +20,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
 
-typedef _Float16 f16;
-typedef f16 f16x2 __attribute__((ext_vector_type(2)));
-typedef f16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kWave = 64;
 constexpr int kWavesPerBlock = 4;
-// Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family GPUs.
-constexpr int kBufferWord3 = 0x00020000;
 constexpr int kBlock = kWave * kWavesPerBlock;
 
-// ---------------------------------------------------------------- helpers
-__device__ __forceinline__ f16x8 stream_load(const f16x8 *p)
-{
-    return __builtin_nontemporal_load(p);
-}
-
-// acc + sum_i a[i] * b[i] over 8 fp16 pairs, as four v_dot2 (fp32 accumulate)
-__device__ __forceinline__ float dot8(f16x8 a, f16x8 b, float acc)
-{
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 0, 1),
-                                 __builtin_shufflevector(b, b, 0, 1), acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 2, 3),
-                                 __builtin_shufflevector(b, b, 2, 3), acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 4, 5),
-                                 __builtin_shufflevector(b, b, 4, 5), acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(a, a, 6, 7),
-                                 __builtin_shufflevector(b, b, 6, 7), acc, false);
-    return acc;
-}
-
-// value of lane (src per DPP_CTRL) for lanes whose row is enabled in ROW_MASK, 0 elsewhere
-template <int DPP_CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp(float v)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                 DPP_CTRL, ROW_MASK, 0xF, false));
-}
-
-// Sum over aligned groups of G lanes (G = 8, 16, 32 or 64), fixed tree:
-//   quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
-//   row_half_mirror (8-lane halves), row_mirror (16-lane rows),
-//   row_bcast:15 (row r-1's last lane into rows 1 and 3),
-//   row_bcast:31 (lane 31 into rows 2 and 3).
-// The group sum is valid in group_holder<G>(g) (and, for G <= 16, in every
-// lane of the group).
-template <int G>
-__device__ __forceinline__ float group_sum(float v)
-{
-    static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group size");
-    v += dpp<0xB1, 0xF>(v);
-    v += dpp<0x4E, 0xF>(v);
-    v += dpp<0x141, 0xF>(v);
-    if (G >= 16) v += dpp<0x140, 0xF>(v);
-    if (G >= 32) v += dpp<0x142, 0xA>(v);
-    if (G >= 64) v += dpp<0x143, 0xC>(v);
-    return v;
-}
-
-template <int G>
-__device__ __forceinline__ int group_holder(int g)
-{
-    return G <= 16 ? g * G : (G == 32 ? g * 32 + 31 : 63);
-}
-
-// Whole-wave sum, returned as a wave-uniform value.
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v = group_sum<64>(v);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
-__device__ __forceinline__ float silu_mul(float g, float u)
-{
-    return g / (1.0f + expf(-g)) * u;
-}
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
-
 // ---------------------------------------------------------------- router GEMV
-// Lane l holds 16-byte chunks c*64 + l of a 2048-wide (H = 512*HC) row.
-template <int HC>
-__device__ __forceinline__ void load_row(const f16 *row, f16x8 (&w)[HC])
-{
-    const f16x8 *r = reinterpret_cast<const f16x8 *>(row);
-#pragma unroll
-    for (int c = 0; c < HC; ++c) w[c] = stream_load(r + c * kWave + lane_id());
-}
-
-template <int HC>
-__device__ __forceinline__ void load_x(const f16 *xrow, f16x8 (&xv)[HC])
-{
-    const f16x8 *r = reinterpret_cast<const f16x8 *>(xrow);
-#pragma unroll
-    for (int c = 0; c < HC; ++c) xv[c] = r[c * kWave + lane_id()];
-}
-
-// sum over the row of w * x: per-lane v_dot2 chain over its chunks, then the wave tree
-template <int HC>
-__device__ __forceinline__ float row_dot(const f16x8 (&w)[HC], const f16x8 (&xv)[HC])
-{
-    float acc = 0.0f;
-#pragma unroll
-    for (int c = 0; c < HC; ++c) acc = dot8(w[c], xv[c], acc);
-    return wave_sum(acc);
-}
-
 // One wave, expert row e: logits[m, e] = sum_h Wr[e, h] x[m, h] for m < M.
 template <int HC>
 __device__ __forceinline__ void router_row(const f16 *__restrict__ x,
@@ -156,148 +54,7 @@ __global__ __launch_bounds__(kWave) void k_router(const f16 *__restrict__ x,
     router_row<HC>(x, wr, M, E, blockIdx.x, logits);
 }
 
-// ---------------------------------------------------------------- top-k + softmax
-// One wave selects for one token.  A finite fp32 logit maps to an
-// order-preserving non-zero uint32 key (0 marks "no entry"); K rounds of a
-// wave-wide DPP max find the largest remaining key, and a ballot over the
-// lane's slots (slot i holds expert i*64 + lane) picks the lowest expert id
-// holding it, so equal logits order by the lower id.
-__device__ __forceinline__ uint32_t order_key(float v)
-{
-    v = v + 0.0f; // -0 -> +0, so the two zeros tie
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_value(uint32_t k)
-{
-    const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-    return __builtin_bit_cast(float, u);
-}
-
-template <int DPP_CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
-{
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_CTRL, ROW_MASK, 0xF, false);
-}
-
-__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
-{
-    v = umax(v, dpp_u32<0xB1, 0xF>(v));
-    v = umax(v, dpp_u32<0x4E, 0xF>(v));
-    v = umax(v, dpp_u32<0x141, 0xF>(v));
-    v = umax(v, dpp_u32<0x140, 0xF>(v));
-    v = umax(v, dpp_u32<0x142, 0xA>(v));
-    v = umax(v, dpp_u32<0x143, 0xC>(v));
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-__device__ __forceinline__ int wave_min_i32(int v)
-{
-    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
-    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
-    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));
-    v = min(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));
-    v = min(v, __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, 0x142, 0xA, 0xF, false));
-    v = min(v, __builtin_amdgcn_update_dpp(0x7FFFFFFF, v, 0x143, 0xC, 0xF, false));
-    return __builtin_amdgcn_readlane(v, 63);
-}
-
-// Top-K over the wave of N (key, id) pairs per lane (key 0 = no entry; ids
-// distinct): lane k < K receives the k-th largest key and its id, equal keys
-// ordered by ascending id.  Each lane first sorts its pairs by descending key,
-// ascending id (odd-even transposition, swapping only strictly out-of-order
-// neighbours: stable for pairs that arrive in ascending id order, and ties
-// between pairs in any order are decided by the id test); then every round
-// takes the largest head key over the wave, the lowest id among the heads
-// holding it (a second reduction only when several lanes tie), and that lane
-// pops its head.
-template <int N>
-__device__ __forceinline__ void wave_topk_keys(uint32_t (&key)[N], int (&id)[N], int K,
-                                               uint32_t &my_key, int &my_id)
-{
-    const int lane = lane_id();
-#pragma unroll
-    for (int r = 0; r < N; ++r)
-#pragma unroll
-        for (int i = r & 1; i + 1 < N; i += 2)
-            if (key[i] < key[i + 1] || (key[i] == key[i + 1] && id[i] > id[i + 1])) {
-                const uint32_t tk = key[i];
-                key[i] = key[i + 1];
-                key[i + 1] = tk;
-                const int ti = id[i];
-                id[i] = id[i + 1];
-                id[i + 1] = ti;
-            }
-    my_key = 0u;
-    my_id = 0;
-    for (int k = 0; k < K; ++k) {
-        const uint32_t m = wave_max_u32(key[0]);
-        const uint64_t b = __ballot(key[0] == m);
-        int winner = __builtin_ctzll(b);
-        int wid = __builtin_amdgcn_readlane(id[0], winner);
-        if (__builtin_popcountll(b) > 1) { // equal keys in several lanes: lowest id first
-            wid = wave_min_i32(key[0] == m ? id[0] : 0x7FFFFFFF);
-            winner = __builtin_ctzll(__ballot(key[0] == m && id[0] == wid));
-        }
-        if (lane == winner) {
-#pragma unroll
-            for (int i = 0; i + 1 < N; ++i) {
-                key[i] = key[i + 1];
-                id[i] = id[i + 1];
-            }
-            key[N - 1] = 0u;
-        }
-        if (lane == k) {
-            my_key = m;
-            my_id = wid;
-        }
-    }
-}
-
-// Top-K of E <= 64*NPL logits held by the wave: v[i] is the logit of expert
-// i*64 + lane (ignored where that is >= E).  Lane k < K receives the k-th
-// selected expert id and its logit; returns the largest logit (wave-uniform).
-template <int NPL>
-__device__ __forceinline__ float wave_topk_vals(const float (&v)[NPL], int E, int K, int &my_id,
-                                                float &my_l)
-{
-    uint32_t key[NPL];
-    int id[NPL];
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-        id[i] = i * kWave + lane_id();
-        key[i] = id[i] < E ? order_key(v[i]) : 0u;
-    }
-    uint32_t my_key;
-    wave_topk_keys<NPL>(key, id, K, my_key, my_id);
-    my_l = my_key ? key_value(my_key) : 0.0f;
-    return key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
-}
-
-// Routing weight of the slot held by this lane (valid in lanes < K): softmax
-// over the selected logits (renormalize) or over all E logits.
-template <int NPL>
-__device__ __forceinline__ float topk_weight_vals(const float (&v)[NPL], int E, int K,
-                                                  int renormalize, float my_l, float lmax)
-{
-    const int lane = lane_id();
-    const float ex = lane < K ? expf(my_l - lmax) : 0.0f;
-    float z;
-    if (renormalize) {
-        z = wave_sum(ex);
-    } else {
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NPL; ++i)
-            if (i * kWave + lane < E) part += expf(v[i] - lmax);
-        z = wave_sum(part);
-    }
-    return ex / z;
-}
-
+// ---------------------------------------------------------------- top-k kernels
 template <int NPL>
 __global__ __launch_bounds__(kWave) void k_topk(const float *__restrict__ logits, int E, int K,
                                                 int renormalize, int32_t *__restrict__ ids,
@@ -525,21 +282,6 @@ __global__ __launch_bounds__(kBlock) void k_w13_multi(const f16 *__restrict__ x,
 }
 
 // ---------------------------------------------------------------- W2 + combine
-// d + sum_i w[i] * a[i] over one 16-byte chunk of a W2 row (8 fp16 weights)
-// and the matching 8 fp32 activations, in element order.
-__device__ __forceinline__ float dot8_f32(f16x8 w, f32x4 a0, f32x4 a1, float d)
-{
-    d = fmaf((float)w[0], a0[0], d);
-    d = fmaf((float)w[1], a0[1], d);
-    d = fmaf((float)w[2], a0[2], d);
-    d = fmaf((float)w[3], a0[3], d);
-    d = fmaf((float)w[4], a1[0], d);
-    d = fmaf((float)w[5], a1[1], d);
-    d = fmaf((float)w[6], a1[2], d);
-    d = fmaf((float)w[7], a1[3], d);
-    return d;
-}
-
 // A wave owns RPL = 64/LPR consecutive output rows h; LPR lanes share one
 // row, each holding CPL 16-byte chunks of it (I = 8*LPR*CPL).  For every
 // selected expert (routing order; for M > 1 the distinct experts in order of
@@ -813,27 +555,6 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
 // The per-element arithmetic is the separate kernels' (the same device
 // functions, lane mappings and reduction trees, in the same order), so the
 // results equal shared_expert + moe_route + moe_decode_fused bit for bit.
-
-// gate row j and up row I + j of the expert at `base` -> silu(gate) * up
-// (the W13 kernel's arithmetic for one token)
-template <int HC>
-__device__ __forceinline__ float w13_pair(const f16 *__restrict__ x, const f16 *__restrict__ base,
-                                          int I, int j)
-{
-    constexpr int H = 512 * HC;
-    f16x8 xv[HC], wg[HC], wu[HC];
-    load_x<HC>(x, xv);
-    const f16x8 *grow = reinterpret_cast<const f16x8 *>(base + (size_t)j * H);
-    const f16x8 *urow = reinterpret_cast<const f16x8 *>(base + (size_t)(I + j) * H);
-#pragma unroll
-    for (int c = 0; c < HC; ++c) {
-        wg[c] = stream_load(grow + c * kWave + lane_id());
-        wu[c] = stream_load(urow + c * kWave + lane_id());
-    }
-    const float g = row_dot<HC>(wg, xv);
-    const float up = row_dot<HC>(wu, xv);
-    return silu_mul(g, up);
-}
 
 // One single-wave workgroup per router row (the router kernel's arithmetic):
 // a layer's router is latency-bound, and 256 small workgroups spread its rows

@@ -100,3 +100,17 @@ def check_y(y, ref_y, where=""):
     assert rel <= Y_REL_L2, "rel-L2 %g > %g %s" % (rel, Y_REL_L2, where)
     assert mx <= Y_MAX_ABS, "max-abs %g > %g %s" % (mx, Y_MAX_ABS, where)
     return rel, mx
+
+
+def single_launch(shape: synth.LayerShape) -> bool:
+    """Whether moe_layer_decode runs these sizes as the single-launch layer on
+    an MI355X (256 CUs in 8 XCDs): the bounds moe_decode.h states for it."""
+    if shape.M != 1 or shape.H not in (1024, 2048) or not 1 <= shape.E <= 256:
+        return False
+    if not 1 <= shape.K <= min(8, shape.E) or shape.I not in (64, 128, 256, 512, 1024):
+        return False
+    if shape.Is not in (0, shape.I) or shape.K * shape.I > 4096:
+        return False
+    rpl = 64 // (64 if shape.I >= 512 else shape.I // 8)
+    rpw = shape.H // 256
+    return rpw % rpl == 0 and rpw // rpl <= 8

@@ -32,7 +32,25 @@ def declared_functions():
 def test_library_builds_and_loads():
     assert os.path.exists(build.LIB) or build.build(force=True)
     L = _lib.lib()
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
+
+
+def test_library_matches_the_sources():
+    L = _lib.lib()
+    assert L.moe_build_id().decode() == build.source_id()
+
+
+def test_stale_library_is_refused(tmp_path, monkeypatch):
+    """A library built from other sources than the tree holds is never loaded:
+    with one source edited (a copy with an extra comment stands in for it),
+    lib() raises instead of handing out the old binary."""
+    src = build.SOURCES[0]
+    edited = tmp_path / os.path.basename(src)
+    edited.write_bytes(open(src, "rb").read() + b"\n// edited after the build\n")
+    monkeypatch.setattr(build, "SOURCES", [str(edited)] + build.SOURCES[1:])
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(_lib.StaleLibraryError):
+        _lib.lib()
 
 
 def test_every_declared_symbol_is_exported():
@@ -196,11 +214,19 @@ def test_layer_stage_probe_validation():
         return L.moe_dbg_layer_stage(stage, FAKE, FAKE, FAKE, FAKE, None, None, M, H, 256, 512, 8,
                                      0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
 
-    assert call(0) == -2 and call(4) == -2
+    assert call(0) == -2 and call(7) == -2 and call(-1) == -2
     assert call(2, M=2) == -2          # not the three-launch path
+    assert call(5, M=2) == -2          # not the single-launch path
     assert call(2, H=2000) == -2
     assert L.moe_dbg_layer_stage(2, None, FAKE, FAKE, FAKE, None, None, 1, 2048, 256, 512, 8, 0, 1,
                                  FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+
+
+def test_workspace_init_validation():
+    L = _lib.lib()
+    assert L.moe_workspace_init(None, 8192, None) == -1
+    assert L.moe_workspace_init(FAKE_ODD, 8192, None) == -3
+    assert L.moe_workspace_init(FAKE, 8191, None) == -4
 
 
 def test_prefill_workspace_bytes():

@@ -1,8 +1,8 @@
 """moe_layer_decode against the three entry points issued one after another.
 
-Both ways of running the layer (three launches at M = 1, else the separate
-kernels) must agree with the three calls bit for bit: routing outputs (ids,
-weights, logits) and y.  The results must also be reproducible call after
+Every way of running the layer (three launches at M = 1, three or four for
+small batches, else the separate kernels) must agree with the three calls
+bit for bit: routing outputs (ids, weights, logits) and y.  The results must also be reproducible call after
 call on the same workspace, equal under graph replay, and within the oracle
 tolerance.
 """
