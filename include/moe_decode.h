@@ -74,6 +74,7 @@ typedef int moe_status;
 #define MOE_ERR_ALIGN (-3)       /* a pointer is not aligned as required */
 #define MOE_ERR_WORKSPACE (-4)   /* ws_bytes < moe_workspace_bytes(...) */
 #define MOE_ERR_HIP (-5)         /* a kernel launch failed (hipGetLastError) */
+#define MOE_ERR_SCRATCH (-6)     /* sizes beyond moe_layer_decode_noalloc's static buffer */
 
 /* ABI version of the loaded library (MOE_ABI_VERSION it was built with). */
 int moe_abi_version(void);
@@ -183,6 +184,24 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
                             const void *w_gate_up, const void *w_down, int M, int H, int E, int I,
                             int K, int Is, int renormalize, int32_t *topk_ids, float *topk_w,
                             float *logits, void *y, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_decode for callers that cannot allocate device memory (code under
+ * hipGraph capture, serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, results and launches, without `ws`.  Its workspace is a static
+ * device buffer of 512 KiB inside the library, one per GPU, held from the
+ * first call on that GPU until the process ends; the call itself allocates
+ * nothing and frees nothing.  Sizes whose moe_workspace_bytes exceeds 512 KiB
+ * (for example M = 8, K = 16, I = 2048) return MOE_ERR_SCRATCH before anything
+ * is enqueued.  The buffer is shared by every call on that GPU and keeps the
+ * last call's contents (the call needs none of it to start at any value):
+ * calls that overlap in time on one GPU, from any stream or thread, race and
+ * must be avoided.  The first call on a device looks the buffer's address up
+ * (thread-safe; not a stream operation).  Other errors as for moe_layer_decode. */
+moe_status moe_layer_decode_noalloc(const void *x, const void *w_router, const void *w13,
+                                    const void *w2, const void *w_gate_up, const void *w_down,
+                                    int M, int H, int E, int I, int K, int Is, int renormalize,
+                                    int32_t *topk_ids, float *topk_w, float *logits, void *y,
+                                    hipStream_t stream);
 
 /* Number of kernels moe_layer_decode enqueues for these sizes (3 at M = 1..4,
  * 4 at M = 5..8), 0 for unsupported sizes or M = 0. */

@@ -13,12 +13,13 @@ _lib = None
 
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
-                -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP"}
+                -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_HIP", -6: "MOE_ERR_SCRATCH"}
 EXPORTED = ["moe_abi_version", "moe_build_id", "moe_status_str", "moe_workspace_bytes", "moe_route",
             "shared_expert", "moe_decode_fused", "moe_dbg_wave_sum", "moe_dbg_w13_silu",
             "moe_dbg_w2_combine", "moe_layer_decode", "moe_layer_launches", "moe_dbg_layer_stage",
             "moe_probe_empty", "moe_probe_read", "moe_probe_copy", "moe_prefill_workspace_bytes",
-            "moe_layer_prefill", "moe_dbg_prefill_stage", "moe_workspace_init"]
+            "moe_layer_prefill", "moe_dbg_prefill_stage", "moe_workspace_init",
+            "moe_layer_decode_noalloc"]
 
 _vp = C.c_void_p
 _i = C.c_int
@@ -85,6 +86,9 @@ def lib() -> C.CDLL:
             L.moe_prefill_workspace_bytes.argtypes = [_i] * 6
             L.moe_layer_prefill.restype = _i
             L.moe_layer_prefill.argtypes = L.moe_layer_decode.argtypes
+            L.moe_layer_decode_noalloc.restype = _i
+            L.moe_layer_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp] + [_i] * 7 + \
+                [_vp, _vp, _vp, _vp, _vp]
             L.moe_workspace_init.restype = _i
             L.moe_workspace_init.argtypes = [_vp, _sz, _vp]
             L.moe_dbg_prefill_stage.restype = _i

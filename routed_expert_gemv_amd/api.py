@@ -246,13 +246,14 @@ def _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_id
         _dev_tensor(name, t, dt)
         if t.numel() != n:
             raise ValueError("%s must have %d elements" % (name, n))
+    args = (_ptr(x), _ptr(w_router), _ptr(w13), _ptr(w2), _ptr(w_gate_up), _ptr(w_down), M, H, E,
+            I, K, Is, int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y))
+    if ws is False:  # the entry point takes no workspace
+        return (y, topk_ids, topk_w, logits), args
     if ws is None:
         ws = (make_ws or workspace)(max(M, 1), H, E, I, K, Is, dev)
     _dev_tensor("ws", ws, torch.uint8)
-    args = (_ptr(x), _ptr(w_router), _ptr(w13), _ptr(w2), _ptr(w_gate_up), _ptr(w_down), M, H, E,
-            I, K, Is, int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_w), _ptr(logits), _ptr(y),
-            _ptr(ws), ws.numel())
-    return (y, topk_ids, topk_w, logits), args
+    return (y, topk_ids, topk_w, logits), args + (_ptr(ws), ws.numel())
 
 
 def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int = 8,
@@ -264,6 +265,19 @@ def moe_layer_decode(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int =
                             topk_w, logits, y, ws)
     st = _lib.lib().moe_layer_decode(*args, _stream(stream, x.device))
     _check("moe_layer_decode", st)
+    return out
+
+
+def moe_layer_decode_noalloc(x, w_router, w13, w2, w_gate_up=None, w_down=None, K: int = 8,
+                             renormalize: bool = True, topk_ids=None, topk_w=None, logits=None,
+                             y=None, stream=None):
+    """moe_layer_decode without a workspace argument: the library's static
+    512 KiB device buffer serves as the workspace (nothing is allocated by the
+    call; calls on one GPU must not overlap).  Returns (y, topk_ids, topk_w, logits)."""
+    out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
+                            topk_w, logits, y, False)
+    st = _lib.lib().moe_layer_decode_noalloc(*args, _stream(stream, x.device))
+    _check("moe_layer_decode_noalloc", st)
     return out
 
 

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_decode.so")
 SOURCES = [os.path.join(CSRC, "moe_kernels.hip"), os.path.join(CSRC, "moe_layer1.hip"),
-           os.path.join(CSRC, "moe_prefill.hip"), os.path.join(CSRC, "moe_abi.cpp")]
+           os.path.join(CSRC, "moe_prefill.hip"), os.path.join(CSRC, "moe_noalloc.hip"),
+           os.path.join(CSRC, "moe_abi.cpp")]
 HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(CSRC, "moe_device.h"),
            os.path.join(INCLUDE, "moe_decode.h"), os.path.join(INCLUDE, "moe_prefill.h")]
 ARCH = "gfx950"

@@ -136,6 +136,7 @@ const char *moe_status_str(moe_status s)
     case MOE_ERR_ALIGN: return "a pointer is not aligned as required";
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
     case MOE_ERR_HIP: return "a kernel launch failed";
+    case MOE_ERR_SCRATCH: return "the sizes need more scratch than the library's static buffer";
     default: return "unknown status";
     }
 }
@@ -198,6 +199,23 @@ moe_status moe_layer_decode(const void *x, const void *w_router, const void *w13
 {
     return layer_decode(x, w_router, w13, w2, w_gate_up, w_down, M, H, E, I, K, Is, renormalize,
                         topk_ids, topk_w, logits, y, ws, ws_bytes, 0, stream);
+}
+
+moe_status moe_layer_decode_noalloc(const void *x, const void *w_router, const void *w13,
+                                    const void *w2, const void *w_gate_up, const void *w_down,
+                                    int M, int H, int E, int I, int K, int Is, int renormalize,
+                                    int32_t *topk_ids, float *topk_w, float *logits, void *y,
+                                    hipStream_t stream)
+{
+    const bool shared = w_gate_up != nullptr || w_down != nullptr;
+    const size_t need = moe_workspace_bytes(M, H, E, I, K, shared ? Is : 0);
+    if (need == 0 || (shared && !i_ok(Is))) return MOE_ERR_SHAPE;
+    if (need > kNoAllocScratchBytes) return MOE_ERR_SCRATCH;
+    if (M == 0) return MOE_OK;
+    void *ws = nullptr;
+    if (noalloc_scratch(&ws) != hipSuccess) return MOE_ERR_HIP;
+    return layer_decode(x, w_router, w13, w2, w_gate_up, w_down, M, H, E, I, K, Is, renormalize,
+                        topk_ids, topk_w, logits, y, ws, kNoAllocScratchBytes, 0, stream);
 }
 
 moe_status moe_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream)

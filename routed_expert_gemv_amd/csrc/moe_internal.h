@@ -125,6 +125,10 @@ hipError_t launch_layer1(const void *x, const void *wr, const void *w13, const v
                          unsigned spin, hipStream_t s);
 constexpr unsigned kLayer1Spin = 1u << 16;
 hipError_t launch_state_clear(void *ws, hipStream_t s);
+// The static device buffer of moe_layer_decode_noalloc (moe_noalloc.hip): its
+// size, and its address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = 512 * 1024;
+hipError_t noalloc_scratch(void **out);
 hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
                        const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
                        int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,

@@ -70,7 +70,7 @@ def test_abi_version_matches_header():
 
 def test_status_strings():
     L = _lib.lib()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = L.moe_status_str(code).decode()
         assert s and s != "unknown status"
     assert L.moe_status_str(-99).decode() == "unknown status"
@@ -220,6 +220,21 @@ def test_layer_stage_probe_validation():
     assert call(2, H=2000) == -2
     assert L.moe_dbg_layer_stage(2, None, FAKE, FAKE, FAKE, None, None, 1, 2048, 256, 512, 8, 0, 1,
                                  FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+
+
+def test_noalloc_validation():
+    """The entry point without a workspace refuses bad sizes, and sizes whose
+    workspace exceeds its static buffer, before touching the device."""
+    L = _lib.lib()
+
+    def call(M=1, H=2048, E=256, I=512, K=8, Is=0, gu=None, d=None):
+        return L.moe_layer_decode_noalloc(FAKE, FAKE, FAKE, FAKE, gu, d, M, H, E, I, K, Is, 1,
+                                          FAKE, FAKE, FAKE, FAKE, None)
+
+    assert call(H=2000) == -2 and call(M=9) == -2 and call(K=0) == -2
+    assert call(M=8, E=1024, I=2048, K=16) == -6          # over 512 KiB of workspace
+    assert call(M=8, I=2048, K=16, Is=2048, gu=FAKE, d=FAKE) == -6
+    assert L.moe_status_str(-6).decode() != "unknown status"
 
 
 def test_workspace_init_validation():
