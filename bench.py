@@ -11,13 +11,17 @@ from HBM.  Inputs are seeded synthetic tensors resident in HBM before timing.
 
 Each layer is one moe_layer_decode call, three launches at M=1 (router +
 shared gate/up, expand, reduce); with --path separate the three entry points
-run instead (six kernels per layer).
+run instead (six kernels per layer).  --shape tp4_shard_e256_k8_i128 runs the
+TP=4 shard of the same layer instead (I=128, shared Is=128: 15.2 MB touched
+per layer, 548 MB per replay, still above the last-level cache); --tokens
+2/4/8 the small-batch layers.
 
 Reported (one JSON line): expert-byte throughput in GB/s (value), us/layer,
 fraction of the 8 TB/s HBM peak, the roofline of the dominant kernel (the
-expand kernel; every kernel of every layer timed with HIP events that the
-library records on the stream the kernels run on) and the fp64 oracle timed on
-this host's cores on a bounded sample of the same layers.
+expand kernel, timed with HIP events over graphs of that kernel alone, next to
+the average of the same graphs in the committed rocprofv3 trace when it was
+taken on the current sources) and the fp64 oracle timed on this host's cores
+(one core and all of them) on a bounded sample of the same layers.
 
 With --prefill T the workload is the many-token layer instead: a stack of
 full-width layers (default 8) with T tokens each, every layer one
@@ -43,6 +47,12 @@ LAYERS = 36
 COUNTERS = os.path.join(ROOT, "profiles", "k_expand_counters_full_e256_k8_i512.json")
 STAGES = ("k_router1", "k_expand", "k_reduce")
 KERNEL_SRC = os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", "moe_kernels.hip")
+# sources the decode kernels are compiled from (a summary taken on other
+# sources no longer describes the kernels that run)
+DECODE_SRCS = tuple(os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", f)
+                    for f in ("moe_kernels.hip", "moe_device.h", "moe_internal.h"))
+DECODE_SHAPES = ("full_e256_k8_i512", "tp4_shard_e256_k8_i128", "batch2_e256_k8_i512",
+                 "batch4_e256_k8_i512", "batch8_e256_k8_i512")
 PF_METRIC = "MoE prefill tokens/s through one full-width layer (T tokens per layer)"
 PF_STAGES = ("k_pf_router", "k_pf_topk", "k_pf_plan", "k_pf_w13", "k_pf_w2", "k_pf_combine")
 PF_KERNEL_SRC = os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", "moe_prefill.hip")
@@ -103,17 +113,45 @@ def prefill_flops(sh):
             "k_pf_w2": 2 * T * (K * I + Is) * H}
 
 
-def counters_traffic(path=COUNTERS, src=KERNEL_SRC):
+def sources_sha(srcs):
+    h = hashlib.sha256()
+    for f in srcs:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def counters_path(shape):
+    return os.path.join(ROOT, "profiles", "k_expand_counters_%s.json" % shape)
+
+
+def trace_path(shape):
+    return os.path.join(ROOT, "profiles", "layer_kernels_trace_%s.md" % shape)
+
+
+def counters_traffic(path=COUNTERS, srcs=DECODE_SRCS):
     """HBM traffic per launch of the summarised kernel from a committed rocprofv3
-    counter summary, if it was taken on the current kernel source; else None."""
+    counter summary, if it was taken on the current kernel sources; else None."""
     try:
         c = json.load(open(path))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if c.get("kernel_source_sha256") != sha:
+    if c.get("kernel_source_sha256") != sources_sha(srcs):
         return None
     return c.get("hbm_bytes_per_dispatch")
+
+
+def rocprof_stage_us(shape):
+    """Per-kernel average duration inside the stage graphs from the committed
+    rocprofv3 kernel-trace summary of this shape (its trailing JSON block), if
+    that trace was taken on the current kernel sources; else None."""
+    try:
+        text = open(trace_path(shape)).read()
+        blob = json.loads(text.rsplit("```json", 1)[1].split("```", 1)[0])
+    except (OSError, ValueError, IndexError):
+        return None
+    if blob.get("kernel_source_sha256") != sources_sha(DECODE_SRCS):
+        return None
+    return blob.get("stage_avg_us")
 
 
 def cpu_model():
@@ -334,7 +372,7 @@ def prefill_main(args, dev):
     k_gbs = st_b[dom] / (st_us[dom] * 1e-6) / 1e9
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-            "traffic": counters_traffic(pf_counters_path(T), PF_KERNEL_SRC),
+            "traffic": counters_traffic(pf_counters_path(T), (PF_KERNEL_SRC,)),
             "avg_launch_us": round(st_us[dom], 3), "bytes_per_launch": st_b[dom],
             "launches_timed": n_launch,
             "mfma_tflops": round(fl[dom] / (st_us[dom] * 1e-6) / 1e12, 1),
@@ -390,8 +428,7 @@ def counters_pass(args):
         sh = synth.LayerShape(M=args.prefill, H=2048, E=256, K=8, I=512, Is=512)
         layers = [PrefillLayer(synth.draw_layer(sh, s, dev), sh) for s in range(args.layers)]
     else:
-        sh = synth.SHAPES["full_e256_k8_i512" if args.tokens == 1 else
-                          "batch%d_e256_k8_i512" % args.tokens]
+        sh = synth.SHAPES[args.shape]
         layers = [DecodeLayer(synth.draw_layer(sh, s, dev), sh) for s in range(args.layers)]
     for _ in range(2):
         for l in layers:
@@ -410,7 +447,7 @@ def _read_csv_rows(d, suffix):
     return rows
 
 
-def summarize_counters(fetch_dir, write_dir, out_path, cmds, prefill=0):
+def summarize_counters(fetch_dir, write_dir, out_path, cmds, prefill=0, shape="full_e256_k8_i512"):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE of the expand kernel (and, for
     context, the other two), scaled by what the same counters read for the
     1 GiB copy, into a JSON summary."""
@@ -444,7 +481,7 @@ def summarize_counters(fetch_dir, write_dir, out_path, cmds, prefill=0):
         algo = prefill_stage_bytes(sh, sh.E)  # every expert receives tokens at this size
         other_names = ("k_pf_router", "k_pf_w2", "k_pf_combine")
     else:
-        sh = synth.SHAPES["full_e256_k8_i512"]
+        sh = synth.SHAPES[shape]
         algo = stage_bytes(sh)
         other_names = ("k_router1", "k_reduce")
     others = {}
@@ -458,10 +495,11 @@ def summarize_counters(fetch_dir, write_dir, out_path, cmds, prefill=0):
     res = {
         "kernel": ("k_pf_w13 (grouped gate/up GEMM + SiLU*mul, routed and shared experts), T=%d"
                    % prefill) if prefill else
-                  "k_expand<4,4,64,1,2> (routed and shared gate/up + SiLU*mul), M=1",
+                  "k_expand (routed and shared gate/up + SiLU*mul), M=1",
         "workload": ("full-width prefill layer H=2048 E=256 K=8 I=512 Is=512, T=%d tokens"
                      % prefill) if prefill else
-                    "full-width layer H=2048 E=256 K=8 I=512 Is=512, M=1, 36 layers rotating",
+                    "%s: H=%d E=%d K=%d I=%d Is=%d, M=1, 36 layers rotating"
+                    % (shape, sh.H, sh.E, sh.K, sh.I, sh.Is),
         "commands": cmds,
         "fetch_size_kib_per_dispatch": sum(fw) / len(fw),
         "write_size_kib_per_dispatch": sum(ww) / len(ww),
@@ -471,17 +509,59 @@ def summarize_counters(fetch_dir, write_dir, out_path, cmds, prefill=0):
         "algorithmic_bytes_per_dispatch": algo[kern],
         "dispatches": len(fw),
         "other_kernels": others,
-        "kernel_source_sha256": hashlib.sha256(open(PF_KERNEL_SRC if prefill else KERNEL_SRC,
-                                                    "rb").read()).hexdigest(),
+        "kernel_source_sha256": sources_sha((PF_KERNEL_SRC,) if prefill else DECODE_SRCS),
     }
     with open(out_path, "w") as fh:
         json.dump(res, fh, indent=1)
     print(json.dumps(res, indent=1))
 
 
-def summarize_trace(trace_dir, out_path, cmd):
-    """Kernel-trace summary: per-kernel count / average duration, and the average
-    idle gap between consecutive kernels inside the replayed stack graph."""
+def summarize_pmc(out_path, dirs, cmds, title):
+    """Average per dispatch of every counter collected in the given rocprofv3
+    --pmc output folders, for each of the library's kernels (one row per
+    kernel and instance), as a markdown table."""
+    vals = {}
+    for d in dirs:
+        for r in _read_csv_rows(d, "counter_collection.csv"):
+            name = r.get("Kernel_Name", "")
+            if not ("_ZN3moe" in name or "moe::" in name):
+                continue
+            key = (kernel_key(name), name)
+            vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    counters = sorted({c for v in vals.values() for c in v})
+    lines = ["# rocprofv3 counters: " + title, ""] + ["Command: `%s`" % c for c in cmds] + [
+        "", "Average per dispatch (dispatches in parentheses).", "",
+        "| kernel | " + " | ".join(counters) + " |", "|---" * (len(counters) + 1) + "|"]
+    for (k, n), v in sorted(vals.items()):
+        tmpl = n[n.find("I", n.find(k) + len(k)):][:40] if "_ZN3moe" in n else ""
+        cells = []
+        for c in counters:
+            x = v.get(c)
+            cells.append("%.4g (%d)" % (sum(x) / len(x), len(x)) if x else "-")
+        lines.append("| `%s` %s | %s |" % (k, ("`" + tmpl + "`") if tmpl else "", " | ".join(cells)))
+    lines += ["", "kernel_source_sha256 (decode sources): " + sources_sha(DECODE_SRCS)]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def kernel_key(name):
+    """The kernel's own name (k_expand, ...) from a mangled or demangled name."""
+    import re
+    m = re.search(r"_ZN3moe(\d+)", name)
+    if m:
+        n = int(m.group(1))
+        return name[m.end():m.end() + n]
+    m = re.search(r"moe::(k_\w+)", name)
+    return m.group(1) if m else name.replace("(anonymous namespace)::", "").split("(")[0][:90]
+
+
+def summarize_trace(trace_dir, out_path, cmd, bench_line=None):
+    """Kernel-trace summary: per-kernel count / average duration, the averages
+    inside the per-kernel stage graphs bench.py times (next to bench.py's own
+    HIP-event figures from the same run, when its output line is given), and the
+    idle gap between consecutive kernels; a trailing JSON block holds the
+    stage-graph averages and the hash of the kernel sources."""
     rows = _read_csv_rows(trace_dir, "kernel_trace.csv")
     if not rows:
         raise SystemExit("no kernel_trace.csv under " + trace_dir)
@@ -498,8 +578,7 @@ def summarize_trace(trace_dir, out_path, cmd):
         return n.replace("(anonymous namespace)::", "").split("(")[0][:90]
 
     for n, d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        short = short_name(n)
-        lines.append("| `%s` | %d | %.3f | %.3f | %.3f |" % (short, len(d), sum(d) / len(d) / 1e3,
+        lines.append("| `%s` | %d | %.3f | %.3f | %.3f |" % (short_name(n), len(d), sum(d) / len(d) / 1e3,
                                                           min(d) / 1e3, max(d) / 1e3))
     # dispatches inside the per-kernel stage graphs that bench times (each
     # neighbour is the same kernel), next to the average over every dispatch
@@ -507,17 +586,34 @@ def summarize_trace(trace_dir, out_path, cmd):
     for i in range(1, len(ours) - 1):
         if ours[i - 1][2] == ours[i][2] == ours[i + 1][2]:
             runs.setdefault(ours[i][2], []).append(ours[i][1] - ours[i][0])
+    line = None
+    if bench_line:
+        for ln in open(bench_line):
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    ev_us = ((line or {}).get("roofline") or {}).get("per_kernel_us", {})
+    stage_avg = {}
     if runs:
-        lines += ["", "Inside the stage graphs (dispatches whose neighbours are the same kernel):", "",
-                  "| kernel | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+        lines += ["", "Inside the stage graphs (dispatches whose neighbours are the same kernel), "
+                      "with bench.py's HIP-event average per launch over the same graphs:", "",
+                  "| kernel | dispatches | avg us | min us | max us | HIP events us |",
+                  "|---|---|---|---|---|---|"]
         for n, d in sorted(runs.items(), key=lambda kv: -sum(kv[1])):
-            lines.append("| `%s` | %d | %.3f | %.3f | %.3f |" % (
-                short_name(n), len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, max(d) / 1e3))
+            k = kernel_key(n)
+            stage_avg[k] = round(sum(d) / len(d) / 1e3, 4)
+            lines.append("| `%s` | %d | %.3f | %.3f | %.3f | %s |" % (
+                short_name(n), len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, max(d) / 1e3,
+                "%.3f" % ev_us[k] if k in ev_us else "-"))
     if gaps:
         gaps.sort()
         lines += ["", "Gap between consecutive library kernels (end -> next start, < 20 us): "
                   "n=%d, median %.3f us, mean %.3f us" % (len(gaps), gaps[len(gaps) // 2] / 1e3,
                                                        sum(gaps) / len(gaps) / 1e3)]
+    if line:
+        lines += ["", "bench.py line of the profiled run: %.3f us/layer, %.1f GB/s (under the "
+                      "profiler)" % (line.get("us_per_layer", 0.0), line.get("value", 0.0))]
+    blob = {"stage_avg_us": stage_avg, "kernel_source_sha256": sources_sha(DECODE_SRCS)}
+    lines += ["", "```json", json.dumps(blob), "```"]
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -586,6 +682,9 @@ def main():
                     help="layers in the stack (decode default %d, prefill default 8)" % LAYERS)
     ap.add_argument("--prefill", type=int, default=0, metavar="T",
                     help="bench the many-token layer with T tokens per layer instead of decode")
+    ap.add_argument("--shape", choices=DECODE_SHAPES, default=None,
+                    help="decode layer shape (default full_e256_k8_i512, or the batch shape "
+                         "--tokens names); tp4_shard_e256_k8_i128 is the TP=4 shard")
     ap.add_argument("--tokens", type=int, default=1, choices=(1, 2, 4, 8),
                     help="tokens per layer: 1 (the default workload) or a small decode batch "
                          "(each token routed on its own; distinct experts read once)")
@@ -600,6 +699,11 @@ def main():
                     help="run the rocprofv3 --pmc workload (copy calibration + layer launches)")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"))
+    ap.add_argument("--bench-line", default=None,
+                    help="file holding the bench.py output of the profiled run (for --summarize-trace)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="OUT_THEN_DIRS",
+                    help="markdown summary OUT of the --pmc output folders that follow")
+    ap.add_argument("--title", default="", help="title of a --summarize-pmc summary")
     ap.add_argument("--cmd", action="append", default=[],
                     help="command line(s) recorded in a summary")
     args = ap.parse_args()
@@ -607,11 +711,22 @@ def main():
     if args.layers is None:
         args.layers = LAYERS
 
+    if args.shape is None:
+        args.shape = "full_e256_k8_i512" if args.tokens == 1 else "batch%d_e256_k8_i512" % args.tokens
+    elif args.tokens != 1:
+        ap.error("--tokens and --shape name the workload twice: give one")
+
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, cmds=args.cmd, prefill=args.prefill)
+        summarize_counters(*args.summarize_counters, cmds=args.cmd, prefill=args.prefill,
+                           shape=args.shape)
         return
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace, cmd=" && ".join(args.cmd))
+        summarize_trace(*args.summarize_trace, cmd=" && ".join(args.cmd), bench_line=args.bench_line)
+        return
+    if args.summarize_pmc:
+        if len(args.summarize_pmc) < 2:
+            ap.error("--summarize-pmc OUT DIR [DIR ...]")
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1:], args.cmd, args.title)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -634,8 +749,7 @@ def main():
     if args.prefill:
         prefill_main(args, dev)
         return
-    sh = synth.SHAPES["full_e256_k8_i512" if args.tokens == 1 else
-                      "batch%d_e256_k8_i512" % args.tokens]
+    sh = synth.SHAPES[args.shape]
 
     log("drawing %d layers (seeds 0..%d) on %s" % (args.layers, args.layers - 1, dev))
     t0 = time.perf_counter()
@@ -680,20 +794,30 @@ def main():
             for k in STAGES)))
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(k_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-                "traffic": counters_traffic() if dom == "k_expand" else None,
+                "traffic": counters_traffic(counters_path(args.shape)) if dom == "k_expand" else None,
                 "avg_launch_us": round(st_us[dom], 3), "bytes_per_launch": st_b[dom],
                 "launches_timed": n_launch,
+                "frac_method": "HIP events around %d replays of a graph of the kernel alone for "
+                               "every layer, divided by the launches" % args.launch_reps,
                 "per_kernel_us": {k: round(v, 3) for k, v in st_us.items()},
                 "per_kernel_bytes": st_b}
+        rp = rocprof_stage_us(args.shape)
+        if rp and dom in rp:
+            # the same stage graphs in the committed rocprofv3 kernel trace
+            roof["rocprof_avg_launch_us"] = rp[dom]
+            roof["rocprof_frac"] = round(st_b[dom] / (rp[dom] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            roof["rocprof_summary"] = os.path.relpath(trace_path(args.shape), ROOT)
 
     out = {
         "metric": METRIC, "value": round(gbs_expert, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": "%d-layer full-width MoE decode stack as one hipGraph: M=%d, "
-                               "H=2048, E=256, top-8 renormalised, I=512, shared Is=512, fp16"
-                               % (args.layers, sh.M),
+        "config": {"workload": "%d-layer %s MoE decode stack as one hipGraph: M=%d, H=%d, E=%d, "
+                               "top-%d renormalised, I=%d, shared Is=%d, fp16"
+                               % (args.layers, "TP=4-shard" if args.shape.startswith("tp4")
+                                  else "full-width", sh.M, sh.H, sh.E, sh.K, sh.I, sh.Is),
+                   "shape": args.shape,
                    "tokens": sh.M,
                    "distinct_experts_per_layer": round(sum(n_distinct) / len(n_distinct), 2),
                    "layers": args.layers, "layer_seeds": "0..%d" % (args.layers - 1),

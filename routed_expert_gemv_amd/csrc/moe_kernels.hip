@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -1237,22 +1239,25 @@ static hipError_t launch_w2_t(const float *act, const void *w2, const int32_t *i
         // comes on top of `lds`
         if (H % rows == 0 && lds + kMaxSlots * 16 <= lds_optin_bytes()) {
             auto kern = k_w2_staged<LPR, CPL, MT, SHARED>;
-            // opt this instance into the device's full LDS, once per device
-            static bool opted[kMaxDevices] = {};
+            // Opt this instance into the device's full LDS once per device,
+            // whatever this call's size: the launch's LDS is the dynamic bytes
+            // plus the kernel's static arrays, and the default 64 KiB limit
+            // applies to that sum.
+            static std::atomic<bool> opted[kMaxDevices] = {};
             int dev = 0;
-            if (lds > 64 * 1024 && hipGetDevice(&dev) == hipSuccess && dev < kMaxDevices &&
-                !opted[dev]) {
-                // dynamic LDS may use what the kernel's static LDS leaves
+            hipError_t e = hipGetDevice(&dev);
+            if (e != hipSuccess) return e;
+            if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+            if (!opted[dev].load(std::memory_order_acquire)) {
                 hipFuncAttributes fa;
-                hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
+                e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
                 if (e != hipSuccess) return e;
                 e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                         hipFuncAttributeMaxDynamicSharedMemorySize,
                                         (int)(lds_optin_bytes() - fa.sharedSizeBytes));
                 if (e != hipSuccess) return e;
-                opted[dev] = true;
+                opted[dev].store(true, std::memory_order_release);
             }
-            if (lds > 64 * 1024 && dev >= kMaxDevices) return hipErrorInvalidDevice;
             hipLaunchKernelGGL(kern, dim3(H / rows), dim3(kSBlock), lds, s, act,
                                (const f16 *)w2, tw, shared_in, M, H, I, K, table, out);
             return last();

@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -499,16 +501,16 @@ template <int HC, int NPL, int LPR, int CPL, int KMAX, bool SH, int PPW>
 hipError_t launch_t(const L1Args &a, hipStream_t s)
 {
     auto kern = k_layer1<HC, NPL, LPR, CPL, KMAX, SH, PPW>;
-    static bool opted[64] = {};
+    static std::atomic<bool> opted[64] = {};
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (!opted[dev]) {
+    if (!opted[dev].load(std::memory_order_acquire)) {
         err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLayer1Lds);
         if (err != hipSuccess) return err;
-        opted[dev] = true;
+        opted[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL(kern, dim3(kLayer1Grid), dim3(kL1Block), kLayer1Lds, s, a);
     return hipGetLastError();

@@ -113,13 +113,20 @@ def test_dot2_keeps_fp16_subnormals_exact():
     ("tiny_e16_k4_i128", [0, 1, 2]),
     ("tp4_shard_e256_k8_i128", [0, 1]),
     ("full_e256_k8_i512", [0, 1]),
-    ("batch2_e256_k8_i512", [0]),
-    ("batch4_e256_k8_i512", [0]),
-    ("batch8_e256_k8_i512", [0]),
+    ("batch2_e256_k8_i512", [0, 1, 2]),
+    ("batch4_e256_k8_i512", [0, 1, 2]),
+    ("batch8_e256_k8_i512", [0, 1, 2]),
 ])
 def test_layer_parity(name, seeds):
     for s in seeds:
         parity(synth.SHAPES[name], s, name)
+
+
+def test_staged_down_kernel_at_64k_lds():
+    """M=4, K=8, I=512: the staged down kernel holds 64 KiB of activations in
+    dynamic LDS next to its static arrays, above the default 64 KiB limit; the
+    calls must succeed (any failed launch status raises) and match the oracle."""
+    parity(synth.SHAPES["batch4_e256_k8_i512"], 7, "staged 64 KiB")
 
 
 @pytest.mark.parametrize("shape", [
