@@ -45,9 +45,14 @@
  *   - M = 0 is a valid empty call: nothing is enqueued, MOE_OK is returned.
  *
  * Supported sizes (MOE_ERR_SHAPE otherwise):
- *   0 <= M <= 8;  H in {512, 1024, 2048, 4096} (H = 4096 needs M <= 4);
+ *   0 <= M <= 8;  H a multiple of 512, 512 <= H <= 4096 (H > 2048 needs M <= 4);
  *   1 <= E <= 1024;  1 <= K <= min(E, 16);
- *   I and Is in {64, 128, 256, 512, 1024, 2048}.
+ *   I and Is multiples of 64, 64 <= I, Is <= 2048.
+ * The kernels reduce a down-projection row of width n (I, or Is) in a lane
+ * mapping chosen by n alone: LPR lanes per row, CPL 16-byte chunks per lane,
+ * n = 8*LPR*CPL exactly where n/8 = LPR*CPL for some LPR in {8, 16, 32, 64}
+ * and CPL <= 4 (for example I = 768: 32 lanes x 3 chunks); any other width
+ * takes 64 lanes with the chunks past the row's end weighted zero.
  * Alignment (MOE_ERR_ALIGN otherwise): fp16 tensors 16 bytes, fp32/int32
  * arrays 4 bytes, workspace 256 bytes.
  */
@@ -62,7 +67,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 #define MOE_MAX_TOKENS 8
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_EXPERTS 1024

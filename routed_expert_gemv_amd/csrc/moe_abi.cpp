@@ -11,9 +11,14 @@ using namespace moe;
 
 namespace {
 
-bool h_ok(int H) { return H == 512 || H == 1024 || H == 2048 || H == 4096; }
-bool i_ok(int I) { return I == 64 || I == 128 || I == 256 || I == 512 || I == 1024 || I == 2048; }
-bool m_ok(int M, int H) { return M >= 0 && M <= kMaxTokens && (H < 4096 || M <= 4); }
+// hidden width: a multiple of 512 up to 4096 (each lane of a wave holds H/512
+// 16-byte chunks of a row); expert widths I, Is: multiples of 64 up to 2048
+// (any such width has a lane mapping of its down-projection rows)
+bool h_ok(int H) { return H >= 512 && H <= 4096 && H % 512 == 0; }
+bool i_ok(int I) { return I >= 64 && I <= kMaxInter && I % 64 == 0; }
+// above H = 2048, x of more than 4 tokens no longer fits the multi-token
+// kernels' registers
+bool m_ok(int M, int H) { return M >= 0 && M <= kMaxTokens && (H <= 2048 || M <= 4); }
 bool ek_ok(int E, int K) { return E >= 1 && E <= kMaxExperts && K >= 1 && K <= kMaxTopk && K <= E; }
 
 bool al(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }

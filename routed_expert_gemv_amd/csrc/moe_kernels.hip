@@ -21,6 +21,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -29,6 +30,47 @@ namespace moe {
 
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = kWave * kWavesPerBlock;
+
+// ---------------------------------------------------------------- lane mappings
+// How a wave covers rows of a down projection (W2 rows, I wide; shared down
+// rows, Is wide; n = 16-byte chunks per row): LPR lanes per row (8, 16, 32 or
+// 64, so a wave holds RPL = 64/LPR rows), each lane loading CPL chunks, chunk
+// q = c*LPR + cl in its c-th step.  A lane's partial sum runs over its chunks
+// in step order, then the group tree of LPR lanes adds the partials.
+// When n = LPR*CPL for some LPR with CPL <= 4 the mapping is exact (the largest
+// such LPR); otherwise PAD: LPR = 64, CPL = ceil(n/64), and a step past the end
+// of the row re-reads the row's last chunk with zero weights, which appends
+// exact zeros to the end of that lane's chain.  The mapping depends on the row
+// width alone, so every kernel that reduces rows of one width adds in one order.
+template <int LPR_, int CPL_, bool PAD_>
+struct LaneMap {
+    static constexpr int LPR = LPR_;
+    static constexpr int CPL = CPL_;
+    static constexpr bool PAD = PAD_;
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "lanes per row");
+    static_assert(CPL >= 1 && CPL <= 4, "chunks per lane");
+    static_assert(!PAD || LPR == 64, "a padded row takes a whole wave");
+};
+// the mapping used where a kernel instance has no down-projection rows
+using NoLaneMap = LaneMap<64, 1, false>;
+
+template <class LM>
+__device__ __forceinline__ int lm_chunk(int c, int cl, int n)
+{
+    const int q = c * LM::LPR + cl;
+    if constexpr (LM::PAD) return q < n ? q : n - 1;
+    return q;
+}
+
+template <class LM>
+__device__ __forceinline__ f16x8 lm_weights(f16x8 w, int c, int cl, int n)
+{
+    if constexpr (LM::PAD) {
+        const f16x8 zero = {};
+        return c * LM::LPR + cl < n ? w : zero;
+    }
+    return w;
+}
 
 // ---------------------------------------------------------------- router GEMV
 // One wave, expert row e: logits[m, e] = sum_h Wr[e, h] x[m, h] for m < M.
@@ -296,13 +338,16 @@ __global__ __launch_bounds__(kBlock) void k_w13_multi(const f16 *__restrict__ x,
 //
 // SHARED: the shared expert's down projection (one expert at `w2`, weight 1,
 // every token, fp32 output without rounding, nothing added).
-template <int LPR, int CPL, int MT, bool SHARED>
+template <class LM, int MT, bool SHARED>
 __global__ __launch_bounds__(kBlock) void k_w2_combine(
     const float *__restrict__ act, const f16 *__restrict__ w2, const int32_t *__restrict__ ids,
     const float *__restrict__ topk_w, const float *__restrict__ shared_in, int M, int H, int I,
     int K, const GroupTable *__restrict__ table, void *__restrict__ out)
 {
+    constexpr int LPR = LM::LPR;
+    constexpr int CPL = LM::CPL;
     constexpr int RPL = kWave / LPR;
+    const int nch = I / 8;
     constexpr int BATCH = 8;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -328,7 +373,8 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
                 const f16x8 *row =
                     reinterpret_cast<const f16x8 *>(w2 + ((size_t)e * H + h) * I);
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
+                for (int c = 0; c < CPL; ++c)
+                    wv[t][c] = lm_weights<LM>(stream_load(row + lm_chunk<LM>(c, cl, nch)), c, cl, nch);
             }
 #pragma unroll
         for (int t = 0; t < BATCH; ++t)
@@ -349,7 +395,7 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
                         float d = 0.0f;
 #pragma unroll
                         for (int c = 0; c < CPL; ++c) {
-                            const f32x4 *ap = reinterpret_cast<const f32x4 *>(a + (c * LPR + cl) * 8);
+                            const f32x4 *ap = reinterpret_cast<const f32x4 *>(a + lm_chunk<LM>(c, cl, nch) * 8);
                             d = dot8_f32(wv[t][c], ap[0], ap[1], d);
                         }
                         acc[m] = fmaf(wt, d, acc[m]);
@@ -384,14 +430,17 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
 constexpr int kSWaves = 8;
 constexpr int kSBlock = kSWaves * kWave;
 
-template <int LPR, int CPL, int MT, bool SHARED>
+template <class LM, int MT, bool SHARED>
 __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     const float *__restrict__ act, const f16 *__restrict__ w2, const float *__restrict__ topk_w,
     const float *__restrict__ shared_in, int M, int H, int I, int K,
     const GroupTable *__restrict__ table, void *__restrict__ out)
 {
     extern __shared__ float lds[];
+    constexpr int LPR = LM::LPR;
+    constexpr int CPL = LM::CPL;
     constexpr int RPL = kWave / LPR;
+    const int nch = I / 8;
     constexpr int BATCH = 8 / CPL; // 16-byte W2 chunks per lane per buffer: 8
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -423,9 +472,11 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
                 ok ? H * I * 2 : 0, kBufferWord3);
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-                wv[buf][t][c] = __builtin_bit_cast(
-                    f16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                               rs, (uint32_t)(h * I + (c * LPR + cl) * 8) * 2, 0, 0));
+                wv[buf][t][c] = lm_weights<LM>(
+                    __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs, (uint32_t)(h * I + lm_chunk<LM>(c, cl, nch) * 8) * 2,
+                                                  0, 0)),
+                    c, cl, nch);
         }
     };
     // A wave's vector loads complete in issue order, so what is staged in LDS
@@ -509,7 +560,7 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
                         float d = 0.0f;
 #pragma unroll
                         for (int c = 0; c < CPL; ++c) {
-                            const f32x4 *ap = reinterpret_cast<const f32x4 *>(a + (c * LPR + cl) * 8);
+                            const f32x4 *ap = reinterpret_cast<const f32x4 *>(a + lm_chunk<LM>(c, cl, nch) * 8);
                             d = dot8_f32(wv[buf][t][c], ap[0], ap[1], d);
                         }
                         acc[m] = fmaf(wt, d, acc[m]);
@@ -602,6 +653,43 @@ __global__ __launch_bounds__(kBlock) void k_router_shared(const f16 *__restrict_
     }
 }
 
+// Wave wi of the shared down projection: rows h = wi*RPL + r (RPL = 64/LPR)
+// for every token, the W2 kernel's arithmetic with weight 1: s[m, h] in fp32.
+template <class LM, int MT>
+__device__ __forceinline__ void shared_down_rows(const f16 *__restrict__ wsd,
+                                                 const float *__restrict__ act_s, int M, int H,
+                                                 int Is, int wi, float *__restrict__ s_out)
+{
+    constexpr int LPR = LM::LPR;
+    constexpr int CPL = LM::CPL;
+    constexpr int RPL = kWave / LPR;
+    const int lane = lane_id();
+    const int r = lane / LPR;
+    const int cl = lane % LPR;
+    const int nch = Is / 8;
+    const int h = wi * RPL + r;
+    const f16x8 *row = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * Is);
+    f16x8 wv[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+        wv[c] = lm_weights<LM>(stream_load(row + lm_chunk<LM>(c, cl, nch)), c, cl, nch);
+    const bool holder = lane == group_holder<LPR>(r);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float d = 0.0f;
+        if (m < M) {
+            const float *am = act_s + (size_t)m * Is;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const f32x4 *ap = reinterpret_cast<const f32x4 *>(am + lm_chunk<LM>(c, cl, nch) * 8);
+                d = dot8_f32(wv[c], ap[0], ap[1], d);
+            }
+        }
+        const float t = group_sum<LPR>(fmaf(1.0f, d, 0.0f));
+        if (m < M && holder) s_out[(size_t)m * H + h] = t;
+    }
+}
+
 // Shared-expert work placed in the expand launch.
 enum : int { kExpandNoShared = 0, kExpandSharedDown = 1, kExpandSharedGateUp = 2 };
 
@@ -616,7 +704,7 @@ enum : int { kExpandNoShared = 0, kExpandSharedDown = 1, kExpandSharedGateUp = 2
 //   kExpandSharedDown    one wave per RPL = 64/LPR rows of the shared down
 //                        projection (wsh = the shared down weights; the W2
 //                        kernel's arithmetic with weight 1) -> s (fp32).
-template <int HC, int NPL, int LPR, int CPL, int SM>
+template <int HC, int NPL, class LM, int SM>
 __global__ __launch_bounds__(kBlock) void k_expand(
     const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsh,
     const float *__restrict__ logits, float *__restrict__ act_s, int E, int I, int K, int Is,
@@ -658,22 +746,8 @@ __global__ __launch_bounds__(kBlock) void k_expand(
         const float a = w13_pair<HC>(x, wsh, Is, j);
         if (lane == 0) act_s[j] = a;
     } else if constexpr (SM == kExpandSharedDown) {
-        constexpr int RPL = kWave / LPR;
-        const int r = lane / LPR;
-        const int cl = lane % LPR;
-        const int h = ((b - routed_blocks) * kWavesPerBlock + wave) * RPL + r;
-        const f16x8 *row = reinterpret_cast<const f16x8 *>(wsh + (size_t)h * Is);
-        f16x8 wv[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) wv[c] = stream_load(row + c * LPR + cl);
-        float d = 0.0f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const f32x4 *ap = reinterpret_cast<const f32x4 *>(act_s + (c * LPR + cl) * 8);
-            d = dot8_f32(wv[c], ap[0], ap[1], d);
-        }
-        const float t = group_sum<LPR>(fmaf(1.0f, d, 0.0f));
-        if (lane == group_holder<LPR>(r)) s_out[h] = t;
+        shared_down_rows<LM, 1>(wsh, act_s, 1, 512 * HC, Is,
+                                (b - routed_blocks) * kWavesPerBlock + wave, s_out);
     }
 }
 
@@ -690,10 +764,10 @@ __global__ __launch_bounds__(kBlock) void k_expand(
 // over row h of the shared down weights and act_s, added as s_in would be.
 constexpr int kRWaves = 8;
 constexpr int kRBlock = kRWaves * kWave;
-constexpr int kMaxStaged = 16384; // K*I fp32 values staged in LDS (64 KB)
+[[maybe_unused]] constexpr int kMaxStaged = 16384; // K*I fp32 values staged in LDS (64 KB)
 
 // STAGE: 16-byte activation loads per thread, ceil(K*I / (4 * kRBlock)).
-template <int LPR, int CPL, int STAGE, bool SH>
+template <class LM, int STAGE, bool SH>
 __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ act,
                                                     const f16 *__restrict__ w2,
                                                     const int32_t *__restrict__ ids,
@@ -707,8 +781,11 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
     // K >= 1 (checked on the host); stated so that the compiler keeps the
     // first batch of loads ahead of the staging barrier
     __builtin_assume(K > 0);
+    constexpr int LPR = LM::LPR;
+    constexpr int CPL = LM::CPL;
     constexpr int RPL = kWave / LPR;
     constexpr int BATCH = 8 / CPL;
+    const int nch = I / 8;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int r = lane / LPR;
@@ -741,10 +818,11 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
     if constexpr (SH) {
         const f16x8 *srow = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * I);
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) sv[c] = stream_load(srow + c * LPR + cl);
+        for (int c = 0; c < CPL; ++c)
+            sv[c] = lm_weights<LM>(stream_load(srow + lm_chunk<LM>(c, cl, nch)), c, cl, nch);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            const f32x4 *ap = reinterpret_cast<const f32x4 *>(act_s + (c * LPR + cl) * 8);
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(act_s + lm_chunk<LM>(c, cl, nch) * 8);
             sa[2 * c] = ap[0];
             sa[2 * c + 1] = ap[1];
         }
@@ -759,7 +837,8 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
             const int e = __builtin_amdgcn_readlane(my_id, k);
             const f16x8 *row = reinterpret_cast<const f16x8 *>(w2 + ((size_t)e * H + h) * I);
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) wv[t][c] = stream_load(row + c * LPR + cl);
+            for (int c = 0; c < CPL; ++c)
+                wv[t][c] = lm_weights<LM>(stream_load(row + lm_chunk<LM>(c, cl, nch)), c, cl, nch);
         }
     };
     load_batch(0);
@@ -782,7 +861,7 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
         float d = 0.0f;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
-            const f32x4 *ap = reinterpret_cast<const f32x4 *>(ak + (c * LPR + cl) * 8);
+            const f32x4 *ap = reinterpret_cast<const f32x4 *>(ak + lm_chunk<LM>(c, cl, nch) * 8);
             d = dot8_f32(wv[t][c], ap[0], ap[1], d);
         }
         return d;
@@ -873,6 +952,7 @@ __device__ __forceinline__ void build_group_table(const int32_t *ids, int M, int
     if (i == kWave) table->n_u = g.n_first0 + __popcll(b);
 }
 
+#if MOE_PART == 0 // kernels that are not templates live in the part that launches them
 __global__ __launch_bounds__(kGroupThreads) void k_group_table(const int32_t *__restrict__ ids,
                                                                int M, int K, int E,
                                                                GroupTable *__restrict__ table)
@@ -880,6 +960,7 @@ __global__ __launch_bounds__(kGroupThreads) void k_group_table(const int32_t *__
     __shared__ GroupScratch g;
     build_group_table(ids, M, K, E, table, g);
 }
+#endif
 
 // ---------------------------------------------------------------- layer path (M > 1)
 // Four launches for a whole layer with 2..8 tokens, the multi-token kernels'
@@ -943,7 +1024,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select_m(const float *__restrict_
 // Routed workgroups: the multi-token W13 work.  Shared workgroups: RPL = 64/LPR
 // rows of the shared down projection per wave for every token (the W2
 // kernel's arithmetic with weight 1), s[m, h] in fp32.
-template <int HC, int MT, int LPR, int CPL>
+template <int HC, int MT, class LM>
 __global__ __launch_bounds__(kBlock) void k_expand_m(const f16 *__restrict__ x,
                                                      const f16 *__restrict__ w13,
                                                      const f16 *__restrict__ wsd,
@@ -959,30 +1040,8 @@ __global__ __launch_bounds__(kBlock) void k_expand_m(const f16 *__restrict__ x,
         w13_multi_block<HC, MT, false>(x, w13, M, I, K, act, table, b, xs);
         return;
     }
-    constexpr int RPL = kWave / LPR;
-    const int lane = lane_id();
-    const int r = lane / LPR;
-    const int cl = lane % LPR;
-    const int h = ((b - routed_blocks) * kWavesPerBlock + threadIdx.x / kWave) * RPL + r;
-    const f16x8 *row = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * Is);
-    f16x8 wv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) wv[c] = stream_load(row + c * LPR + cl);
-    const bool holder = lane == group_holder<LPR>(r);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        float d = 0.0f;
-        if (m < M) {
-            const float *am = act_s + (size_t)m * Is;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const f32x4 *ap = reinterpret_cast<const f32x4 *>(am + (c * LPR + cl) * 8);
-                d = dot8_f32(wv[c], ap[0], ap[1], d);
-            }
-        }
-        const float t = group_sum<LPR>(fmaf(1.0f, d, 0.0f));
-        if (m < M && holder) s_out[(size_t)m * H + h] = t;
-    }
+    shared_down_rows<LM, MT>(wsd, act_s, M, H, Is,
+                             (b - routed_blocks) * kWavesPerBlock + threadIdx.x / kWave, s_out);
 }
 
 // k_expand_m with the selection folded in (M <= 4, one wave per token): every
@@ -992,7 +1051,7 @@ __global__ __launch_bounds__(kBlock) void k_expand_m(const f16 *__restrict__ x,
 // weights and the table that the W2 kernel reads.  The shared workgroups are
 // k_expand_m's.  (At M = 8 each wave would select for two tokens in turn, and
 // the selection launch is kept.)
-template <int HC, int MT, int LPR, int CPL, int NPL>
+template <int HC, int MT, class LM, int NPL>
 __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
     const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsd,
     const float *__restrict__ act_s, const float *__restrict__ logits, int M, int H, int E, int I,
@@ -1038,32 +1097,12 @@ __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
         w13_multi_block<HC, MT, false>(x, w13, M, I, K, act, &tl, b, xs);
         return;
     }
-    constexpr int RPL = kWave / LPR;
-    const int r = lane / LPR;
-    const int cl = lane % LPR;
-    const int h = ((b - routed_blocks) * kWavesPerBlock + threadIdx.x / kWave) * RPL + r;
-    const f16x8 *row = reinterpret_cast<const f16x8 *>(wsd + (size_t)h * Is);
-    f16x8 wv[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) wv[c] = stream_load(row + c * LPR + cl);
-    const bool holder = lane == group_holder<LPR>(r);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        float d = 0.0f;
-        if (m < M) {
-            const float *am = act_s + (size_t)m * Is;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const f32x4 *ap = reinterpret_cast<const f32x4 *>(am + (c * LPR + cl) * 8);
-                d = dot8_f32(wv[c], ap[0], ap[1], d);
-            }
-        }
-        const float t = group_sum<LPR>(fmaf(1.0f, d, 0.0f));
-        if (m < M && holder) s_out[(size_t)m * H + h] = t;
-    }
+    shared_down_rows<LM, MT>(wsd, act_s, M, H, Is,
+                             (b - routed_blocks) * kWavesPerBlock + threadIdx.x / kWave, s_out);
 }
 
 // ---------------------------------------------------------------- probes
+#if MOE_PART == 0
 // empty kernel (launch latency and graph node gap)
 __global__ void k_probe_empty() {}
 
@@ -1111,30 +1150,136 @@ __global__ __launch_bounds__(kWave) void k_dbg_wave_sum(const float *__restrict_
     const float t = wave_sum(in[lane_id()]);
     if (lane_id() == 0) out[0] = t;
 }
+#endif
 
 // ---------------------------------------------------------------- launchers
+// The host side is compiled as several translation units of this one file
+// (MOE_PART, set by the build), so that the kernel instances compile in
+// parallel; every kernel instance belongs to exactly one part:
+//   part 0       the entry points of moe_internal.h, top-k, grouping, probes,
+//                and the dispatch on the hidden width H and on the row widths
+//   parts 1..8   the kernels of hidden width H = 512 * part (router, gate/up,
+//                the expand launches of the layer paths)
+//   parts 9..21  the down-projection kernels (W2 + combine, reduce) of one
+//                lane mapping each, in LaneMaps order
+#ifndef MOE_PART
+#error "moe_kernels.hip is compiled once per part: -DMOE_PART=0..21"
+#endif
+
 static inline hipError_t last() { return hipGetLastError(); }
 
-template <int HC>
-static hipError_t launch_router_hc(const void *x, const void *wr, int M, int E, float *logits,
-                                   hipStream_t s)
+template <class... T>
+struct TypeList {};
+template <int N, class L>
+struct TypeAt;
+template <int N, class T0, class... T>
+struct TypeAt<N, TypeList<T0, T...>> : TypeAt<N - 1, TypeList<T...>> {};
+template <class T0, class... T>
+struct TypeAt<0, TypeList<T0, T...>> {
+    using type = T0;
+};
+using LaneMaps = TypeList<LaneMap<8, 1, false>, LaneMap<16, 1, false>, LaneMap<8, 3, false>,
+                          LaneMap<32, 1, false>, LaneMap<16, 3, false>, LaneMap<64, 1, false>,
+                          LaneMap<32, 3, false>, LaneMap<64, 2, false>, LaneMap<64, 4, false>,
+                          LaneMap<64, 1, true>, LaneMap<64, 2, true>, LaneMap<64, 3, true>,
+                          LaneMap<64, 4, true>>;
+#define MOE_FIRST_LANE_PART 9 // parts MOE_FIRST_LANE_PART .. +12: LaneMaps[part - 9]
+#define MOE_LAST_PART 21
+
+// f(LaneMap) with the lane mapping of rows n fp16 wide (n % 64 == 0, 64 <= n
+// <= 2048, as the entry points require): exact where n/8 = LPR*CPL, LPR in
+// {8, 16, 32, 64}, CPL <= 4 (largest LPR), padded 64-lane rows otherwise.
+template <class F>
+static auto with_lane_map(int n, F &&f) -> decltype(f(NoLaneMap{}))
 {
-    hipLaunchKernelGGL(k_router<HC>, dim3(E), dim3(kWave), 0, s, (const f16 *)x,
-                       (const f16 *)wr, M, E, logits);
-    return last();
+    switch (n / 8) {
+    case 8: return f(LaneMap<8, 1, false>{});
+    case 16: return f(LaneMap<16, 1, false>{});
+    case 24: return f(LaneMap<8, 3, false>{});
+    case 32: return f(LaneMap<32, 1, false>{});
+    case 48: return f(LaneMap<16, 3, false>{});
+    case 64: return f(LaneMap<64, 1, false>{});
+    case 96: return f(LaneMap<32, 3, false>{});
+    case 128: return f(LaneMap<64, 2, false>{});
+    case 256: return f(LaneMap<64, 4, false>{});
+    }
+    switch ((n / 8 + kWave - 1) / kWave) {
+    case 1: return f(LaneMap<64, 1, true>{});
+    case 2: return f(LaneMap<64, 2, true>{});
+    case 3: return f(LaneMap<64, 3, true>{});
+    default: return f(LaneMap<64, 4, true>{});
+    }
 }
 
+// lanes per row of the mapping of rows n fp16 wide
+static inline int lpr_of(int n)
+{
+    return with_lane_map(n, [](auto lm) { return decltype(lm)::LPR; });
+}
+
+template <int N>
+using IntC = std::integral_constant<int, N>;
+
+// f(IntC<HC>) for H = 512 * HC, HC = 1..8
+template <class F>
+static hipError_t with_hc(int H, F &&f)
+{
+    switch (H / 512) {
+    case 1: return f(IntC<1>{});
+    case 2: return f(IntC<2>{});
+    case 3: return f(IntC<3>{});
+    case 4: return f(IntC<4>{});
+    case 5: return f(IntC<5>{});
+    case 6: return f(IntC<6>{});
+    case 7: return f(IntC<7>{});
+    case 8: return f(IntC<8>{});
+    }
+    return hipErrorInvalidValue;
+}
+
+// Where a layer's shared-expert work goes (the three-launch path): with
+// Is == I the shared down projection shares the routed one's lane mapping,
+// so its gate/up rows stream in k_expand and its down rows in k_reduce;
+// otherwise gate/up beside the router and down in k_expand.
+static inline bool shared_folded(int I, int Is) { return Is == I; }
+
+// ---- per-H entry points (defined in part H/512)
+template <int HC>
+hipError_t hc_router(const void *x, const void *wr, int M, int E, float *logits, hipStream_t s);
+template <int HC>
+hipError_t hc_w13(bool shared, const void *x, const void *w13, const int32_t *ids, int M, int I,
+                  int K, int n_slots, float *act, GroupTable *table, hipStream_t s);
+template <int HC>
+hipError_t hc_lean(const void *x, const void *wr, const void *w13, const void *wsgu,
+                   const void *wsd, int E, int I, int K, int Is, int renorm, int32_t *ids,
+                   float *w, float *logits, float *act, float *act_s, float *s_out, int stage,
+                   hipStream_t s);
+template <int HC>
+hipError_t hc_lean_m(const void *x, const void *wr, const void *w13, const void *wsgu,
+                     const void *wsd, int M, int E, int I, int K, int Is, int renorm,
+                     int32_t *ids, float *w, float *logits, float *act, float *act_s,
+                     float *s_out, GroupTable *table, hipStream_t s);
+// ---- per-lane-mapping entry points (defined in the part of that mapping)
+template <class LM>
+hipError_t lm_w2(bool shared, const float *act, const void *w2, const int32_t *ids,
+                 const float *tw, const float *shared_in, int M, int H, int I, int K,
+                 const GroupTable *table, void *out, hipStream_t s);
+template <class LM>
+hipError_t lm_reduce(const float *act, const void *w2, const int32_t *ids, const float *w,
+                     const float *s_in, const void *wsd, const float *act_s, bool shared, int H,
+                     int I, int K, void *y, hipStream_t s);
+// ---- part 0
+hipError_t launch_select_m(const float *logits, int M, int E, int K, int renorm, int32_t *ids,
+                           float *w, GroupTable *table, hipStream_t s);
+
+#if MOE_PART == 0
+// ================================================================ part 0
 hipError_t launch_route(const void *x, const void *wr, int M, int H, int E, int K, int renorm,
                         int32_t *ids, float *w, float *logits, hipStream_t s)
 {
-    hipError_t err;
-    switch (H / 512) {
-    case 1: err = launch_router_hc<1>(x, wr, M, E, logits, s); break;
-    case 2: err = launch_router_hc<2>(x, wr, M, E, logits, s); break;
-    case 4: err = launch_router_hc<4>(x, wr, M, E, logits, s); break;
-    case 8: err = launch_router_hc<8>(x, wr, M, E, logits, s); break;
-    default: return hipErrorInvalidValue;
-    }
+    hipError_t err = with_hc(H, [&](auto hc) {
+        return hc_router<decltype(hc)::value>(x, wr, M, E, logits, s);
+    });
     if (err != hipSuccess) return err;
     return launch_topk(logits, M, E, K, renorm, ids, w, s);
 }
@@ -1167,146 +1312,46 @@ hipError_t launch_topk_sum(const float *part, int P, int M, int E, int K, int re
     return last();
 }
 
-template <int HC, int MT, bool SHARED>
-static hipError_t launch_w13_t(const void *x, const void *w13, const int32_t *ids, int M, int I,
-                               int K, int n_slots, float *act, GroupTable *table, hipStream_t s)
+hipError_t launch_select_m(const float *logits, int M, int E, int K, int renorm, int32_t *ids,
+                           float *w, GroupTable *table, hipStream_t s)
 {
-    if constexpr (MT == 1) {
-        const int blocks = n_slots * (I / kWavesPerBlock);
-        hipLaunchKernelGGL((k_w13_silu<HC, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
-                           (const f16 *)x, (const f16 *)w13, ids, I, act);
-    } else {
-        const int blocks = n_slots * (I / (rows_per_wave_m<SHARED>() * kWavesPerBlock));
-        hipLaunchKernelGGL((k_w13_multi<HC, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
-                           (const f16 *)x, (const f16 *)w13, M, I, K, act, table);
-    }
+    if (E <= kWave)
+        hipLaunchKernelGGL(k_select_m<1>, dim3(1), dim3(kSelBlock), 0, s, logits, M, E, K, renorm,
+                           ids, w, table);
+    else if (E <= 4 * kWave)
+        hipLaunchKernelGGL(k_select_m<4>, dim3(1), dim3(kSelBlock), 0, s, logits, M, E, K, renorm,
+                           ids, w, table);
+    else
+        hipLaunchKernelGGL(k_select_m<kMaxExperts / kWave>, dim3(1), dim3(kSelBlock), 0, s, logits,
+                           M, E, K, renorm, ids, w, table);
     return last();
 }
 
-template <int HC, bool SHARED>
-static hipError_t launch_w13_hc(const void *x, const void *w13, const int32_t *ids, int M, int I,
-                                int K, int n_slots, float *act, GroupTable *table, hipStream_t s)
+static hipError_t launch_w13(bool shared, const void *x, const void *w13, const int32_t *ids,
+                             int M, int H, int I, int K, int n_slots, float *act,
+                             GroupTable *table, hipStream_t s)
 {
-    switch (mt_of(M)) {
-    case 1: return launch_w13_t<HC, 1, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
-    case 2: return launch_w13_t<HC, 2, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
-    case 4: return launch_w13_t<HC, 4, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
-    case 8:
-        if constexpr (HC <= 4)
-            return launch_w13_t<HC, 8, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
-        return hipErrorInvalidValue;
-    }
-    return hipErrorInvalidValue;
+    return with_hc(H, [&](auto hc) {
+        return hc_w13<decltype(hc)::value>(shared, x, w13, ids, M, I, K, n_slots, act, table, s);
+    });
 }
 
-template <bool SHARED>
-static hipError_t launch_w13(const void *x, const void *w13, const int32_t *ids, int M, int H,
-                             int I, int K, int n_slots, float *act, GroupTable *table,
-                             hipStream_t s)
-{
-    switch (H / 512) {
-    case 1: return launch_w13_hc<1, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
-    case 2: return launch_w13_hc<2, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
-    case 4: return launch_w13_hc<4, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
-    case 8: return launch_w13_hc<8, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-constexpr int kMaxDevices = 64;
-
-// Largest dynamic LDS a workgroup may opt into on the current device.
-static size_t lds_optin_bytes()
-{
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess ||
-        v <= 0)
-        return 64 * 1024;
-    return (size_t)v;
-}
-
-template <int LPR, int CPL, int MT, bool SHARED>
-static hipError_t launch_w2_t(const float *act, const void *w2, const int32_t *ids,
-                              const float *tw, const float *shared_in, int M, int H, int I, int K,
-                              const GroupTable *table, void *out, hipStream_t s)
-{
-    if constexpr (MT > 1) {
-        // several tokens: stage the activations in LDS when they fit
-        const size_t lds = (size_t)M * (SHARED ? 1 : K) * I * sizeof(float);
-        constexpr int rows = (kWave / LPR) * kSWaves;
-        // the kernel's static LDS (routing weights, table masks and slots)
-        // comes on top of `lds`
-        if (H % rows == 0 && lds + kMaxSlots * 16 <= lds_optin_bytes()) {
-            auto kern = k_w2_staged<LPR, CPL, MT, SHARED>;
-            // Opt this instance into the device's full LDS once per device,
-            // whatever this call's size: the launch's LDS is the dynamic bytes
-            // plus the kernel's static arrays, and the default 64 KiB limit
-            // applies to that sum.
-            static std::atomic<bool> opted[kMaxDevices] = {};
-            int dev = 0;
-            hipError_t e = hipGetDevice(&dev);
-            if (e != hipSuccess) return e;
-            if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-            if (!opted[dev].load(std::memory_order_acquire)) {
-                hipFuncAttributes fa;
-                e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
-                if (e != hipSuccess) return e;
-                e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        (int)(lds_optin_bytes() - fa.sharedSizeBytes));
-                if (e != hipSuccess) return e;
-                opted[dev].store(true, std::memory_order_release);
-            }
-            hipLaunchKernelGGL(kern, dim3(H / rows), dim3(kSBlock), lds, s, act,
-                               (const f16 *)w2, tw, shared_in, M, H, I, K, table, out);
-            return last();
-        }
-    }
-    constexpr int rows_per_block = (kWave / LPR) * kWavesPerBlock;
-    const int blocks = H / rows_per_block;
-    hipLaunchKernelGGL((k_w2_combine<LPR, CPL, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
-                       act, (const f16 *)w2, ids, tw, shared_in, M, H, I, K, table, out);
-    return last();
-}
-
-template <int LPR, int CPL, bool SHARED>
-static hipError_t launch_w2_i(const float *act, const void *w2, const int32_t *ids,
-                              const float *tw, const float *shared_in, int M, int H, int I, int K,
-                              const GroupTable *table, void *out, hipStream_t s)
-{
-    switch (mt_of(M)) {
-    case 1: return launch_w2_t<LPR, CPL, 1, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    case 2: return launch_w2_t<LPR, CPL, 2, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    case 4: return launch_w2_t<LPR, CPL, 4, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    case 8: return launch_w2_t<LPR, CPL, 8, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <bool SHARED>
-static hipError_t launch_w2(const float *act, const void *w2, const int32_t *ids, const float *tw,
-                            const float *shared_in, int M, int H, int I, int K,
+static hipError_t launch_w2(bool shared, const float *act, const void *w2, const int32_t *ids,
+                            const float *tw, const float *shared_in, int M, int H, int I, int K,
                             const GroupTable *table, void *out, hipStream_t s)
 {
-    switch (I) {
-    case 64: return launch_w2_i<8, 1, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    case 128: return launch_w2_i<16, 1, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    case 256: return launch_w2_i<32, 1, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    case 512: return launch_w2_i<64, 1, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    case 1024: return launch_w2_i<64, 2, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    case 2048: return launch_w2_i<64, 4, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
-    }
-    return hipErrorInvalidValue;
+    return with_lane_map(I, [&](auto lm) {
+        return lm_w2<decltype(lm)>(shared, act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
+    });
 }
 
 hipError_t launch_shared(const void *x, const void *wgu, const void *wd, int M, int H, int Is,
                          float *s_out, float *act_shared, hipStream_t s)
 {
-    hipError_t err = launch_w13<true>(x, wgu, nullptr, M, H, Is, 1, 1, act_shared, nullptr, s);
+    hipError_t err = launch_w13(true, x, wgu, nullptr, M, H, Is, 1, 1, act_shared, nullptr, s);
     if (err != hipSuccess) return err;
-    return launch_w2<true>(act_shared, wd, nullptr, nullptr, nullptr, M, H, Is, 1, nullptr, s_out,
-                           s);
+    return launch_w2(true, act_shared, wd, nullptr, nullptr, nullptr, M, H, Is, 1, nullptr, s_out,
+                     s);
 }
 
 // For M > 1: the distinct selected experts, read by the W13 and W2 kernels.
@@ -1325,7 +1370,7 @@ hipError_t launch_w13_routed(const void *x, const void *w13, const int32_t *ids,
         if (err != hipSuccess) return err;
     }
     const int n_slots = M * K < E ? M * K : E;
-    return launch_w13<false>(x, w13, ids, M, H, I, K, n_slots, act, table, s);
+    return launch_w13(false, x, w13, ids, M, H, I, K, n_slots, act, table, s);
 }
 
 hipError_t launch_fused(const void *x, const void *w13, const void *w2, const int32_t *ids,
@@ -1334,7 +1379,7 @@ hipError_t launch_fused(const void *x, const void *w13, const void *w2, const in
 {
     hipError_t err = launch_w13_routed(x, w13, ids, M, H, E, I, K, act, table, s);
     if (err != hipSuccess) return err;
-    return launch_w2<false>(act, w2, ids, tw, shared_in, M, H, I, K, table, y, s);
+    return launch_w2(false, act, w2, ids, tw, shared_in, M, H, I, K, table, y, s);
 }
 
 hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids, const float *tw,
@@ -1345,7 +1390,7 @@ hipError_t launch_w2_routed(const float *act, const void *w2, const int32_t *ids
         const hipError_t err = launch_group_table(ids, M, K, E, table, s);
         if (err != hipSuccess) return err;
     }
-    return launch_w2<false>(act, w2, ids, tw, shared_in, M, H, I, K, table, y, s);
+    return launch_w2(false, act, w2, ids, tw, shared_in, M, H, I, K, table, y, s);
 }
 
 hipError_t launch_probe_empty(hipStream_t s)
@@ -1380,11 +1425,6 @@ hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s)
     return last();
 }
 
-
-// ---------------------------------------------------------------- layer path launchers
-// lanes per row of a down-projection GEMV over rows of length n (16-byte chunks)
-static inline int lpr_of(int n) { return n >= 512 ? 64 : n / 8; }
-
 bool lean_ok(int M, int H, int E, int I, int K, int Is)
 {
     // k_reduce stages [K*I] fp32 in LDS; its workgroups and k_expand's shared
@@ -1394,21 +1434,107 @@ bool lean_ok(int M, int H, int E, int I, int K, int Is)
            (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
 }
 
-// Where a layer's shared-expert work goes (the three-launch path): with
-// Is == I the shared down projection shares the routed one's lane mapping,
-// so its gate/up rows stream in k_expand and its down rows in k_reduce;
-// otherwise gate/up beside the router and down in k_expand.
-static inline bool shared_folded(int I, int Is) { return Is == I; }
+bool lean_m_ok(int M, int H, int E, int I, int K, int Is)
+{
+    (void)E;
+    (void)I;
+    (void)K;
+    return M >= 2 && M <= kMaxTokens && (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
+}
 
-template <int HC, int NPL, int LPR, int CPL, int SM>
+hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const void *w2,
+                         const void *wsgu, const void *wsd, int M, int H, int E, int I, int K,
+                         int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
+                         float *act, float *act_s, float *s_out, GroupTable *table, hipStream_t s)
+{
+    const hipError_t err = with_hc(H, [&](auto hc) {
+        return hc_lean_m<decltype(hc)::value>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids,
+                                              w, logits, act, act_s, s_out, table, s);
+    });
+    if (err != hipSuccess) return err;
+    return launch_w2(false, act, w2, ids, w, Is ? s_out : nullptr, M, H, I, K, table, y, s);
+}
+
+hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
+                       const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
+                       int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
+                       float *act_s, float *s_out, int stage, hipStream_t s)
+{
+    // stage 0: the three launches; 1, 2, 3: that launch alone
+    if (stage < 0 || stage > 3) return hipErrorInvalidValue;
+    if (stage <= 2) {
+        const hipError_t err = with_hc(H, [&](auto hc) {
+            return hc_lean<decltype(hc)::value>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids,
+                                                w, logits, act, act_s, s_out, stage, s);
+        });
+        if (err != hipSuccess || stage != 0) return err;
+    }
+    const bool folded = Is != 0 && shared_folded(I, Is);
+    const float *s_in = Is && !folded ? s_out : nullptr;
+    return with_lane_map(I, [&](auto lm) {
+        return lm_reduce<decltype(lm)>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
+    });
+}
+
+#elif MOE_PART >= 1 && MOE_PART <= 8
+// ================================================================ parts 1..8: H = 512 * MOE_PART
+template <int HC>
+hipError_t hc_router(const void *x, const void *wr, int M, int E, float *logits, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_router<HC>, dim3(E), dim3(kWave), 0, s, (const f16 *)x,
+                       (const f16 *)wr, M, E, logits);
+    return last();
+}
+
+template <int HC, int MT, bool SHARED>
+static hipError_t launch_w13_t(const void *x, const void *w13, const int32_t *ids, int M, int I,
+                               int K, int n_slots, float *act, GroupTable *table, hipStream_t s)
+{
+    if constexpr (MT == 1) {
+        const int blocks = n_slots * (I / kWavesPerBlock);
+        hipLaunchKernelGGL((k_w13_silu<HC, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
+                           (const f16 *)x, (const f16 *)w13, ids, I, act);
+    } else {
+        const int blocks = n_slots * (I / (rows_per_wave_m<SHARED>() * kWavesPerBlock));
+        hipLaunchKernelGGL((k_w13_multi<HC, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
+                           (const f16 *)x, (const f16 *)w13, M, I, K, act, table);
+    }
+    return last();
+}
+
+template <int HC, bool SHARED>
+static hipError_t launch_w13_mt(const void *x, const void *w13, const int32_t *ids, int M, int I,
+                                int K, int n_slots, float *act, GroupTable *table, hipStream_t s)
+{
+    switch (mt_of(M)) {
+    case 1: return launch_w13_t<HC, 1, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
+    case 2: return launch_w13_t<HC, 2, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
+    case 4: return launch_w13_t<HC, 4, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
+    case 8:
+        if constexpr (HC <= 4)
+            return launch_w13_t<HC, 8, SHARED>(x, w13, ids, M, I, K, n_slots, act, table, s);
+        return hipErrorInvalidValue;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int HC>
+hipError_t hc_w13(bool shared, const void *x, const void *w13, const int32_t *ids, int M, int I,
+                  int K, int n_slots, float *act, GroupTable *table, hipStream_t s)
+{
+    return shared ? launch_w13_mt<HC, true>(x, w13, ids, M, I, K, n_slots, act, table, s)
+                  : launch_w13_mt<HC, false>(x, w13, ids, M, I, K, n_slots, act, table, s);
+}
+
+template <int HC, int NPL, class LM, int SM>
 static void launch_expand_t(dim3 grid, const void *x, const void *w13, const void *wsh,
                             const float *logits, float *act_s, int E, int I, int K, int Is,
                             int renorm, int32_t *ids, float *w, float *act, float *s_out,
                             hipStream_t s)
 {
-    hipLaunchKernelGGL((k_expand<HC, NPL, LPR, CPL, SM>), grid, dim3(kBlock), 0, s,
-                       (const f16 *)x, (const f16 *)w13, (const f16 *)wsh, logits, act_s, E, I,
-                       K, Is, renorm, ids, w, act, s_out);
+    hipLaunchKernelGGL((k_expand<HC, NPL, LM, SM>), grid, dim3(kBlock), 0, s, (const f16 *)x,
+                       (const f16 *)w13, (const f16 *)wsh, logits, act_s, E, I, K, Is, renorm,
+                       ids, w, act, s_out);
 }
 
 template <int HC, int NPL>
@@ -1418,30 +1544,25 @@ static void launch_expand_n(dim3 grid, const void *x, const void *w13, const voi
                             float *s_out, hipStream_t s)
 {
     if (Is == 0) {
-        launch_expand_t<HC, NPL, 64, 1, kExpandNoShared>(grid, x, w13, nullptr, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+        launch_expand_t<HC, NPL, NoLaneMap, kExpandNoShared>(grid, x, w13, nullptr, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
         return;
     }
     if (shared_folded(I, Is)) {
-        launch_expand_t<HC, NPL, 64, 1, kExpandSharedGateUp>(grid, x, w13, wsgu, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+        launch_expand_t<HC, NPL, NoLaneMap, kExpandSharedGateUp>(grid, x, w13, wsgu, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
         return;
     }
-    // the shared down projection's lane mapping (rows of length Is)
-    constexpr int D = kExpandSharedDown;
-    switch (Is) {
-    case 512: launch_expand_t<HC, NPL, 64, 1, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    case 64: launch_expand_t<HC, NPL, 8, 1, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    case 128: launch_expand_t<HC, NPL, 16, 1, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    case 256: launch_expand_t<HC, NPL, 32, 1, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    case 1024: launch_expand_t<HC, NPL, 64, 2, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    default: launch_expand_t<HC, NPL, 64, 4, D>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s); break;
-    }
+    // the shared down projection with the lane mapping of rows Is wide
+    with_lane_map(Is, [&](auto lm) {
+        launch_expand_t<HC, NPL, decltype(lm), kExpandSharedDown>(grid, x, w13, wsd, logits, act_s, E, I, K, Is, renorm, ids, w, act, s_out, s);
+        return 0;
+    });
 }
 
 template <int HC>
-static hipError_t launch_lean_hc(const void *x, const void *wr, const void *w13, const void *wsgu,
-                                 const void *wsd, int E, int I, int K, int Is, int renorm,
-                                 int32_t *ids, float *w, float *logits, float *act, float *act_s,
-                                 float *s_out, int stage, hipStream_t s)
+hipError_t hc_lean(const void *x, const void *wr, const void *w13, const void *wsgu,
+                   const void *wsd, int E, int I, int K, int Is, int renorm, int32_t *ids,
+                   float *w, float *logits, float *act, float *act_s, float *s_out, int stage,
+                   hipStream_t s)
 {
     constexpr int H = 512 * HC;
     const bool router_only = Is == 0 || shared_folded(I, Is);
@@ -1472,60 +1593,15 @@ static hipError_t launch_lean_hc(const void *x, const void *wr, const void *w13,
     return last();
 }
 
-template <int LPR, int CPL, bool SH>
-static void launch_reduce_s(dim3 grid, size_t lds, int stage, const float *act, const f16 *w2,
-                            const int32_t *ids, const float *w, const float *s_in, const f16 *wsd,
-                            const float *act_s, int H, int I, int K, f16 *y, hipStream_t s)
-{
-    const dim3 block(kRBlock);
-    if (stage <= 1)
-        hipLaunchKernelGGL((k_reduce<LPR, CPL, 1, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
-    else if (stage <= 2)
-        hipLaunchKernelGGL((k_reduce<LPR, CPL, 2, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
-    else if (stage <= 4)
-        hipLaunchKernelGGL((k_reduce<LPR, CPL, 4, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
-    else
-        hipLaunchKernelGGL((k_reduce<LPR, CPL, 8, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
-}
-
-// shared: the shared down projection runs here (wsd, act_s), else s_in (or
-// nullptr without a shared expert) is added
-template <int LPR, int CPL>
-static hipError_t launch_reduce_t(const float *act, const void *w2, const int32_t *ids,
-                                  const float *w, const float *s_in, const void *wsd,
-                                  const float *act_s, bool shared, int H, int I, int K, void *y,
-                                  hipStream_t s)
-{
-    constexpr int rows = kRWaves * (kWave / LPR);
-    const size_t lds = (size_t)K * I * sizeof(float);
-    const int stage = (K * I / 4 + kRBlock - 1) / kRBlock;
-    const dim3 grid(H / rows);
-    if (shared)
-        launch_reduce_s<LPR, CPL, true>(grid, lds, stage, act, (const f16 *)w2, ids, w, nullptr,
-                                        (const f16 *)wsd, act_s, H, I, K, (f16 *)y, s);
-    else
-        launch_reduce_s<LPR, CPL, false>(grid, lds, stage, act, (const f16 *)w2, ids, w, s_in,
-                                         nullptr, nullptr, H, I, K, (f16 *)y, s);
-    return last();
-}
-
-bool lean_m_ok(int M, int H, int E, int I, int K, int Is)
-{
-    (void)E;
-    (void)I;
-    (void)K;
-    return M >= 2 && M <= kMaxTokens && (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
-}
-
-template <int HC, int MT, int LPR, int CPL>
+template <int HC, int MT, class LM>
 static hipError_t launch_expand_m_t(const void *x, const void *w13, const void *wsd,
                                     const float *act_s, int M, int I, int K, int Is, int n_slots,
                                     float *act, float *s_out, const GroupTable *table, hipStream_t s)
 {
     constexpr int H = 512 * HC;
     const int routed = n_slots * (I / (rows_per_wave_m<false>() * kWavesPerBlock));
-    const int shared = Is ? H / (kWavesPerBlock * (kWave / LPR)) : 0;
-    hipLaunchKernelGGL((k_expand_m<HC, MT, LPR, CPL>), dim3(routed + shared), dim3(kBlock), 0, s,
+    const int shared = Is ? H / (kWavesPerBlock * (kWave / LM::LPR)) : 0;
+    hipLaunchKernelGGL((k_expand_m<HC, MT, LM>), dim3(routed + shared), dim3(kBlock), 0, s,
                        (const f16 *)x, (const f16 *)w13, (const f16 *)wsd, act_s, M, H, I, K, Is,
                        routed, act, s_out, table);
     return last();
@@ -1544,64 +1620,40 @@ static hipError_t launch_lean_m_t(const void *x, const void *wr, const void *w13
                        act_s);
     hipError_t err = last();
     if (err != hipSuccess) return err;
+    const int n_slots = M * K < E ? M * K : E;
+    // without a shared expert the mapping is unused (no shared workgroups)
+    const int lm_width = Is ? Is : 512;
     if constexpr (MT <= kWavesPerBlock) {
         // the selection folded into the expand launch (one wave per token)
-        const int n_slots = M * K < E ? M * K : E;
         constexpr int H = 512 * HC;
         const int routed = n_slots * (I / (rows_per_wave_m<false>() * kWavesPerBlock));
-        const int shared = Is ? H / (kWavesPerBlock * (kWave / lpr_of(Is))) : 0;
-        const dim3 grid(routed + shared);
-#define SEL_LAUNCH(LPR_, CPL_, NPL_)                                                              \
-    hipLaunchKernelGGL((k_expand_sel_m<HC, MT, LPR_, CPL_, NPL_>), grid, dim3(kBlock), 0, s,      \
+        return with_lane_map(lm_width, [&](auto lm) {
+            using LM = decltype(lm);
+            const int shared = Is ? H / (kWavesPerBlock * (kWave / LM::LPR)) : 0;
+            const dim3 grid(routed + shared);
+#define SEL_LAUNCH(NPL_)                                                                          \
+    hipLaunchKernelGGL((k_expand_sel_m<HC, MT, LM, NPL_>), grid, dim3(kBlock), 0, s,              \
                        (const f16 *)x, (const f16 *)w13, (const f16 *)wsd, act_s, logits, M, H, E, \
                        I, K, Is, renorm, routed, ids, w, act, s_out, table)
-#define SEL_NPL(LPR_, CPL_)                                                                       \
-    do {                                                                                          \
-        if (E <= kWave) SEL_LAUNCH(LPR_, CPL_, 1);                                                \
-        else if (E <= 4 * kWave) SEL_LAUNCH(LPR_, CPL_, 4);                                       \
-        else SEL_LAUNCH(LPR_, CPL_, kMaxExperts / kWave);                                         \
-    } while (0)
-        switch (Is) {
-        case 0:
-        case 512: SEL_NPL(64, 1); break;
-        case 64: SEL_NPL(8, 1); break;
-        case 128: SEL_NPL(16, 1); break;
-        case 256: SEL_NPL(32, 1); break;
-        case 1024: SEL_NPL(64, 2); break;
-        default: SEL_NPL(64, 4); break;
-        }
-#undef SEL_NPL
+            if (E <= kWave) SEL_LAUNCH(1);
+            else if (E <= 4 * kWave) SEL_LAUNCH(4);
+            else SEL_LAUNCH(kMaxExperts / kWave);
 #undef SEL_LAUNCH
-        return last();
+            return last();
+        });
     }
-    if (E <= kWave)
-        hipLaunchKernelGGL(k_select_m<1>, dim3(1), dim3(kSelBlock), 0, s, logits, M, E, K, renorm,
-                           ids, w, table);
-    else if (E <= 4 * kWave)
-        hipLaunchKernelGGL(k_select_m<4>, dim3(1), dim3(kSelBlock), 0, s, logits, M, E, K, renorm,
-                           ids, w, table);
-    else
-        hipLaunchKernelGGL(k_select_m<kMaxExperts / kWave>, dim3(1), dim3(kSelBlock), 0, s, logits,
-                           M, E, K, renorm, ids, w, table);
-    if ((err = last()) != hipSuccess) return err;
-    const int n_slots = M * K < E ? M * K : E;
-    switch (Is) {
-    case 0:
-    case 512: return launch_expand_m_t<HC, MT, 64, 1>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
-    case 64: return launch_expand_m_t<HC, MT, 8, 1>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
-    case 128: return launch_expand_m_t<HC, MT, 16, 1>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
-    case 256: return launch_expand_m_t<HC, MT, 32, 1>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
-    case 1024: return launch_expand_m_t<HC, MT, 64, 2>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
-    default: return launch_expand_m_t<HC, MT, 64, 4>(x, w13, wsd, act_s, M, I, K, Is, n_slots, act, s_out, table, s);
-    }
+    if ((err = launch_select_m(logits, M, E, K, renorm, ids, w, table, s)) != hipSuccess) return err;
+    return with_lane_map(lm_width, [&](auto lm) {
+        return launch_expand_m_t<HC, MT, decltype(lm)>(x, w13, wsd, act_s, M, I, K, Is, n_slots,
+                                                       act, s_out, table, s);
+    });
 }
 
 template <int HC>
-static hipError_t launch_lean_m_hc(const void *x, const void *wr, const void *w13,
-                                   const void *wsgu, const void *wsd, int M, int E, int I, int K,
-                                   int Is, int renorm, int32_t *ids, float *w, float *logits,
-                                   float *act, float *act_s, float *s_out, GroupTable *table,
-                                   hipStream_t s)
+hipError_t hc_lean_m(const void *x, const void *wr, const void *w13, const void *wsgu,
+                     const void *wsd, int M, int E, int I, int K, int Is, int renorm,
+                     int32_t *ids, float *w, float *logits, float *act, float *act_s,
+                     float *s_out, GroupTable *table, hipStream_t s)
 {
     switch (mt_of(M)) {
     case 2: return launch_lean_m_t<HC, 2>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s);
@@ -1614,52 +1666,144 @@ static hipError_t launch_lean_m_hc(const void *x, const void *wr, const void *w1
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const void *w2,
-                         const void *wsgu, const void *wsd, int M, int H, int E, int I, int K,
-                         int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
-                         float *act, float *act_s, float *s_out, GroupTable *table, hipStream_t s)
+template hipError_t hc_router<MOE_PART>(const void *, const void *, int, int, float *, hipStream_t);
+template hipError_t hc_w13<MOE_PART>(bool, const void *, const void *, const int32_t *, int, int,
+                                     int, int, float *, GroupTable *, hipStream_t);
+template hipError_t hc_lean<MOE_PART>(const void *, const void *, const void *, const void *,
+                                      const void *, int, int, int, int, int, int32_t *, float *,
+                                      float *, float *, float *, float *, int, hipStream_t);
+template hipError_t hc_lean_m<MOE_PART>(const void *, const void *, const void *, const void *,
+                                        const void *, int, int, int, int, int, int, int32_t *,
+                                        float *, float *, float *, float *, float *, GroupTable *,
+                                        hipStream_t);
+
+#elif MOE_PART >= MOE_FIRST_LANE_PART && MOE_PART <= MOE_LAST_PART
+// ================================================================ parts 9..21: one lane mapping
+constexpr int kMaxDevices = 64;
+
+// Largest dynamic LDS a workgroup may opt into on the current device.
+static size_t lds_optin_bytes()
 {
-    hipError_t err;
-    switch (H / 512) {
-    case 1: err = launch_lean_m_hc<1>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s); break;
-    case 2: err = launch_lean_m_hc<2>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s); break;
-    case 4: err = launch_lean_m_hc<4>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s); break;
-    case 8: err = launch_lean_m_hc<8>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s); break;
-    default: return hipErrorInvalidValue;
-    }
-    if (err != hipSuccess) return err;
-    return launch_w2<false>(act, w2, ids, w, Is ? s_out : nullptr, M, H, I, K, table, y, s);
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess ||
+        v <= 0)
+        return 64 * 1024;
+    return (size_t)v;
 }
 
-hipError_t launch_lean(const void *x, const void *wr, const void *w13, const void *w2,
-                       const void *wsgu, const void *wsd, int H, int E, int I, int K, int Is,
-                       int renorm, int32_t *ids, float *w, float *logits, void *y, float *act,
-                       float *act_s, float *s_out, int stage, hipStream_t s)
+template <class LM, int MT, bool SHARED>
+static hipError_t launch_w2_t(const float *act, const void *w2, const int32_t *ids,
+                              const float *tw, const float *shared_in, int M, int H, int I, int K,
+                              const GroupTable *table, void *out, hipStream_t s)
 {
-    // stage 0: the three launches; 1, 2, 3: that launch alone
-    if (stage < 0 || stage > 3) return hipErrorInvalidValue;
-    hipError_t err = hipSuccess;
-    if (stage <= 2) {
-        switch (H / 512) {
-        case 1: err = launch_lean_hc<1>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, stage, s); break;
-        case 2: err = launch_lean_hc<2>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, stage, s); break;
-        case 4: err = launch_lean_hc<4>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, stage, s); break;
-        case 8: err = launch_lean_hc<8>(x, wr, w13, wsgu, wsd, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, stage, s); break;
-        default: return hipErrorInvalidValue;
+    if constexpr (MT > 1) {
+        // several tokens: stage the activations in LDS when they fit
+        const size_t lds = (size_t)M * (SHARED ? 1 : K) * I * sizeof(float);
+        constexpr int rows = (kWave / LM::LPR) * kSWaves;
+        // the kernel's static LDS (routing weights, table masks and slots)
+        // comes on top of `lds`
+        if (H % rows == 0 && lds + kMaxSlots * 16 <= lds_optin_bytes()) {
+            auto kern = k_w2_staged<LM, MT, SHARED>;
+            // Opt this instance into the device's full LDS once per device,
+            // whatever this call's size: the launch's LDS is the dynamic bytes
+            // plus the kernel's static arrays, and the default 64 KiB limit
+            // applies to that sum.
+            static std::atomic<bool> opted[kMaxDevices] = {};
+            int dev = 0;
+            hipError_t e = hipGetDevice(&dev);
+            if (e != hipSuccess) return e;
+            if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+            if (!opted[dev].load(std::memory_order_acquire)) {
+                hipFuncAttributes fa;
+                e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(kern));
+                if (e != hipSuccess) return e;
+                e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        (int)(lds_optin_bytes() - fa.sharedSizeBytes));
+                if (e != hipSuccess) return e;
+                opted[dev].store(true, std::memory_order_release);
+            }
+            hipLaunchKernelGGL(kern, dim3(H / rows), dim3(kSBlock), lds, s, act,
+                               (const f16 *)w2, tw, shared_in, M, H, I, K, table, out);
+            return last();
         }
-        if (err != hipSuccess || stage != 0) return err;
     }
-    const bool folded = Is != 0 && shared_folded(I, Is);
-    const float *s_in = Is && !folded ? s_out : nullptr;
-    switch (I) {
-    case 64: return launch_reduce_t<8, 1>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
-    case 128: return launch_reduce_t<16, 1>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
-    case 256: return launch_reduce_t<32, 1>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
-    case 512: return launch_reduce_t<64, 1>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
-    case 1024: return launch_reduce_t<64, 2>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
-    case 2048: return launch_reduce_t<64, 4>(act, w2, ids, w, s_in, wsd, act_s, folded, H, I, K, y, s);
+    constexpr int rows_per_block = (kWave / LM::LPR) * kWavesPerBlock;
+    const int blocks = H / rows_per_block;
+    hipLaunchKernelGGL((k_w2_combine<LM, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s, act,
+                       (const f16 *)w2, ids, tw, shared_in, M, H, I, K, table, out);
+    return last();
+}
+
+template <class LM, bool SHARED>
+static hipError_t launch_w2_mt(const float *act, const void *w2, const int32_t *ids,
+                               const float *tw, const float *shared_in, int M, int H, int I, int K,
+                               const GroupTable *table, void *out, hipStream_t s)
+{
+    switch (mt_of(M)) {
+    case 1: return launch_w2_t<LM, 1, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
+    case 2: return launch_w2_t<LM, 2, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
+    case 4: return launch_w2_t<LM, 4, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
+    case 8: return launch_w2_t<LM, 8, SHARED>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
     }
     return hipErrorInvalidValue;
 }
+
+template <class LM>
+hipError_t lm_w2(bool shared, const float *act, const void *w2, const int32_t *ids,
+                 const float *tw, const float *shared_in, int M, int H, int I, int K,
+                 const GroupTable *table, void *out, hipStream_t s)
+{
+    return shared ? launch_w2_mt<LM, true>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s)
+                  : launch_w2_mt<LM, false>(act, w2, ids, tw, shared_in, M, H, I, K, table, out, s);
+}
+
+template <class LM, bool SH>
+static void launch_reduce_s(dim3 grid, size_t lds, int stage, const float *act, const f16 *w2,
+                            const int32_t *ids, const float *w, const float *s_in, const f16 *wsd,
+                            const float *act_s, int H, int I, int K, f16 *y, hipStream_t s)
+{
+    const dim3 block(kRBlock);
+    if (stage <= 1)
+        hipLaunchKernelGGL((k_reduce<LM, 1, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+    else if (stage <= 2)
+        hipLaunchKernelGGL((k_reduce<LM, 2, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+    else if (stage <= 4)
+        hipLaunchKernelGGL((k_reduce<LM, 4, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+    else
+        hipLaunchKernelGGL((k_reduce<LM, 8, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+}
+
+// shared: the shared down projection runs here (wsd, act_s), else s_in (or
+// nullptr without a shared expert) is added
+template <class LM>
+hipError_t lm_reduce(const float *act, const void *w2, const int32_t *ids, const float *w,
+                     const float *s_in, const void *wsd, const float *act_s, bool shared, int H,
+                     int I, int K, void *y, hipStream_t s)
+{
+    constexpr int rows = kRWaves * (kWave / LM::LPR);
+    const size_t lds = (size_t)K * I * sizeof(float);
+    const int stage = (K * I / 4 + kRBlock - 1) / kRBlock;
+    const dim3 grid(H / rows);
+    if (shared)
+        launch_reduce_s<LM, true>(grid, lds, stage, act, (const f16 *)w2, ids, w, nullptr,
+                                  (const f16 *)wsd, act_s, H, I, K, (f16 *)y, s);
+    else
+        launch_reduce_s<LM, false>(grid, lds, stage, act, (const f16 *)w2, ids, w, s_in, nullptr,
+                                   nullptr, H, I, K, (f16 *)y, s);
+    return last();
+}
+
+using PartLM = TypeAt<MOE_PART - MOE_FIRST_LANE_PART, LaneMaps>::type;
+template hipError_t lm_w2<PartLM>(bool, const float *, const void *, const int32_t *,
+                                  const float *, const float *, int, int, int, int,
+                                  const GroupTable *, void *, hipStream_t);
+template hipError_t lm_reduce<PartLM>(const float *, const void *, const int32_t *, const float *,
+                                      const float *, const void *, const float *, bool, int, int,
+                                      int, void *, hipStream_t);
+#else
+#error "MOE_PART out of range"
+#endif
 
 } // namespace moe

@@ -29,6 +29,24 @@ Y_MAX_ABS = 2e-2
 MAX_ATTEMPTS = 64
 
 
+# Widths away from the powers of two: H = 512*HC for HC = 3, 5, 6, 7, and
+# down-projection rows with an exact three-chunk lane mapping (I = 192: 8 lanes,
+# 384: 16, 768: 32) or a padded one (320, 448, 576, 704, 960, 1088, 1536, 1984).
+WIDE_SHAPES = [
+    synth.LayerShape(M=1, H=2048, E=128, K=8, I=768, Is=768),
+    synth.LayerShape(M=1, H=2048, E=128, K=8, I=768, Is=0),
+    synth.LayerShape(M=4, H=3072, E=64, K=8, I=192, Is=192),
+    synth.LayerShape(M=1, H=1536, E=32, K=4, I=320, Is=448),
+    synth.LayerShape(M=2, H=2560, E=64, K=6, I=960, Is=1088),
+    synth.LayerShape(M=8, H=1536, E=256, K=8, I=1536, Is=0),
+    synth.LayerShape(M=3, H=3584, E=16, K=4, I=384, Is=640),
+    synth.LayerShape(M=1, H=4096, E=64, K=8, I=1984, Is=1984),
+    synth.LayerShape(M=5, H=1024, E=32, K=5, I=576, Is=576),
+    synth.LayerShape(M=1, H=2560, E=256, K=8, I=384, Is=384),
+    synth.LayerShape(M=7, H=1536, E=48, K=7, I=704, Is=0),
+]
+
+
 def host64(t):
     return None if t is None else t.detach().to("cpu", torch.float64).numpy()
 

@@ -32,7 +32,7 @@ def declared_functions():
 def test_library_builds_and_loads():
     assert os.path.exists(build.LIB) or build.build(force=True)
     L = _lib.lib()
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
 
 
 def test_library_matches_the_sources():
@@ -86,6 +86,59 @@ def test_workspace_bytes():
     assert L.moe_workspace_bytes(1, 2048, 256, 500, 8, 512) == 0      # I
     assert L.moe_workspace_bytes(1, 2048, 4, 512, 8, 0) == 0          # K > E
     assert L.moe_workspace_bytes(8, 4096, 256, 512, 8, 0) == 0        # H = 4096 needs M <= 4
+
+
+# The decode boundary: H a multiple of 512 up to 4096 (M <= 4 above 2048);
+# I and Is multiples of 64 up to 2048.
+H_ACCEPT = list(range(512, 4097, 512))
+H_REJECT = [0, 256, 768, 1000, 2000, 4608, 8192]
+I_ACCEPT = list(range(64, 2049, 64))
+I_REJECT = [0, 32, 96, 100, 200, 992, 2112, 4096]
+
+
+def test_decode_boundary_accept_and_reject_sets():
+    """Every decode entry point takes exactly the widths above.  An accepted
+    shape passes validation and stops at the null x (-1); a rejected one
+    stops at the shape check (-2); neither reaches a launch."""
+    L = _lib.lib()
+
+    def route(M=1, H=2048):
+        return L.moe_route(None, FAKE, M, H, 256, 8, 1, FAKE, FAKE, FAKE, None)
+
+    def shared(M=1, H=2048, Is=512):
+        return L.shared_expert(None, FAKE, FAKE, M, H, Is, FAKE, FAKE, 1 << 30, None)
+
+    def fused(M=1, H=2048, I=512):
+        return L.moe_decode_fused(None, FAKE, FAKE, FAKE, FAKE, None, M, H, 256, I, 8, FAKE, FAKE,
+                                  1 << 30, None)
+
+    def layer(M=1, H=2048, I=512, Is=512):
+        gu = FAKE if Is else None
+        return L.moe_layer_decode(None, FAKE, FAKE, FAKE, gu, gu, M, H, 256, I, 8, Is, 1, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+
+    def ws(M=1, H=2048, I=512, Is=512):
+        return L.moe_workspace_bytes(M, H, 256, I, 8, Is)
+
+    for H in H_ACCEPT:
+        for M in (1, 4):
+            assert route(M, H) == shared(M, H) == fused(M, H) == layer(M, H) == -1, (M, H)
+            assert ws(M, H) > 0
+        m5 = -1 if H <= 2048 else -2       # 5..8 tokens only up to H = 2048
+        assert route(5, H) == shared(5, H) == fused(5, H) == layer(5, H) == m5, H
+        assert (ws(8, H) > 0) == (H <= 2048)
+    for H in H_REJECT:
+        assert route(1, H) == shared(1, H) == fused(1, H) == layer(1, H) == -2, H
+        assert ws(1, H) == 0
+    for I in I_ACCEPT:
+        assert fused(I=I) == shared(Is=I) == layer(I=I, Is=I) == -1, I
+        assert layer(I=I, Is=0) == layer(I=512, Is=I) == layer(M=3, I=I, Is=192) == -1, I
+        assert ws(I=I, Is=I) > 0 and ws(M=8, I=I, Is=0) > 0
+    for I in I_REJECT:
+        assert fused(I=I) == layer(I=I, Is=512) == -2, I
+        assert ws(I=I) == 0
+        if I:  # Is = 0 means "no shared expert" where the entry point allows it
+            assert shared(Is=I) == layer(I=512, Is=I) == -2, I
 
 
 def test_route_validation():

@@ -38,7 +38,7 @@ SHAPES = [
     synth.LayerShape(M=3, H=2048, E=1024, K=16, I=64, Is=64),
     # the same entry point runs the separate kernels
     synth.LayerShape(M=1, H=2048, E=16, K=16, I=2048, Is=0),        # K*I above the LDS stage
-]
+] + cases.WIDE_SHAPES
 
 
 def _id(s):

@@ -144,6 +144,12 @@ def test_edge_shapes(shape):
     parity(shape, 3, "edge")
 
 
+@pytest.mark.parametrize("shape", cases.WIDE_SHAPES,
+                         ids=lambda s: "M%d_H%d_E%d_K%d_I%d_Is%d" % (s.M, s.H, s.E, s.K, s.I, s.Is))
+def test_widths_off_the_powers_of_two(shape):
+    parity(shape, 4, "wide")
+
+
 def test_shared_expert_alone():
     sh = synth.SHAPES["full_e256_k8_i512"]
     say("shared expert alone", sh)
