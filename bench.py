@@ -689,9 +689,9 @@ def main():
                     help="tokens per layer: 1 (the default workload) or a small decode batch "
                          "(each token routed on its own; distinct experts read once)")
     ap.add_argument("--launch-reps", type=int, default=10)
-    ap.add_argument("--path", choices=("fused", "separate"), default="fused",
+    ap.add_argument("--path", choices=("fused", "separate", "single"), default="fused",
                     help="fused: moe_layer_decode (three launches per layer); separate: the "
-                         "three entry points")
+                         "three entry points; single: the single-launch layer (M = 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -754,7 +754,10 @@ def main():
     log("drawing %d layers (seeds 0..%d) on %s" % (args.layers, args.layers - 1, dev))
     t0 = time.perf_counter()
     tensors = [synth.draw_layer(sh, s, dev) for s in range(args.layers)]
-    layers = [DecodeLayer(t, sh, fused=args.path == "fused") for t in tensors]
+    if args.path == "single" and sh.M != 1:
+        ap.error("--path single runs one token per layer")
+    layers = [DecodeLayer(t, sh, fused=args.path != "separate", single=args.path == "single")
+              for t in tensors]
     torch.cuda.synchronize()
     log("drawn in %.1f s; capturing the stack graph" % (time.perf_counter() - t0))
     stack = DecodeStack(layers)
@@ -784,7 +787,15 @@ def main():
     log("%.3f ms/replay, %.2f us/layer, %.0f GB/s expert bytes" % (ms_step, us_layer, gbs_expert))
 
     roof = None
-    if args.path == "fused" and sh.M == 1:
+    if args.path == "single":
+        # one kernel per layer: its launch is the layer
+        k_gbs = total_b / (ms_step * 1e-3) / 1e9
+        roof = {"kernel": "k_layer1", "bound": "hbm", "achieved": round(k_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None, "avg_launch_us": round(us_layer, 3),
+                "bytes_per_launch": total_b // args.layers, "launches_timed": args.steps * args.layers,
+                "frac_method": "HIP events around the stack replays; one launch per layer"}
+    elif args.path == "fused" and sh.M == 1:
         st_us, n_launch = time_stages(layers, args.launch_reps)
         st_b = stage_bytes(sh)
         dom = max(STAGES, key=lambda k: st_us[k])

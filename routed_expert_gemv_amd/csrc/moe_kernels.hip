@@ -207,14 +207,17 @@ __global__ __launch_bounds__(kBlock) void k_w13_silu(const f16 *__restrict__ x,
 
 // The same for M > 1 tokens.  The distinct selected experts U (with each
 // one's token mask and slots) come from the group table; a workgroup takes
-// expert u and 4 row pairs per wave (rows j0 + i*4, the next pair's loads
-// issued before the current pair's arithmetic).  x [M, H] is staged in LDS once per workgroup; for every token
-// that routes to the expert: act[m, slot, j] = silu(gate . x_m) * (up . x_m),
-// the single-token arithmetic.
-// SHARED: the shared expert (every token, slot 0, one "expert" at w13), one
-// row pair per wave so that its single expert still spreads over the chip.
-template <bool SHARED>
-constexpr int rows_per_wave_m() { return SHARED ? 1 : 4; } // the shared expert: more workgroups
+// expert u and R row pairs per wave (rows j0 + i*4, the next pair's loads
+// issued before the current pair's arithmetic).  x [M, H] is staged in LDS
+// once per workgroup; for every token that routes to the expert:
+// act[m, slot, j] = silu(gate . x_m) * (up . x_m), the single-token arithmetic.
+// SHARED: the shared expert (every token, slot 0, one "expert" at w13).
+// Row pairs per wave R: the shared expert one (its single expert still spreads
+// over the chip); routed experts 4 at 3..4 tokens and 2 otherwise (measured in
+// one process with the replays interleaved: 4 pairs against 2 give M = 2
+// 27.74 / 27.50, M = 4 43.92 / 45.77, M = 8 76.96 / 75.56 µs per layer).
+template <bool SHARED, int MT>
+constexpr int rows_per_wave_m() { return SHARED ? 1 : MT == 4 ? 4 : 2; }
 
 // Workgroup b of the multi-token W13 work (xs: LDS for x, MT*HC*64 chunks).
 template <int HC, int MT, bool SHARED>
@@ -225,7 +228,7 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
                                                 f16x8 *xs)
 {
     constexpr int H = 512 * HC;
-    constexpr int kRowsPerWaveM = rows_per_wave_m<SHARED>();
+    constexpr int kRowsPerWaveM = rows_per_wave_m<SHARED, MT>();
     constexpr int kRowsPerBlockM = kRowsPerWaveM * kWavesPerBlock;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -249,7 +252,8 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
         for (int m = 0; m < MT; ++m) slot[m] = table_slot(table, u, m);
     }
     const f16 *base = w13 + (size_t)expert * 2 * I * H;
-    f16x8 wg[2][HC], wu[2][HC];
+    constexpr int D = kRowsPerWaveM < 2 ? kRowsPerWaveM : 2; // row pairs in flight
+    f16x8 wg[D][HC], wu[D][HC];
     auto load_pair = [&](int i, int buf) {
         const int j = j0 + i * kWavesPerBlock;
         const f16x8 *grow = reinterpret_cast<const f16x8 *>(base + (size_t)j * H);
@@ -274,7 +278,9 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
         st[i] = x16[q < n16 ? q : n16 - 1];
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_pair(0, 0);
+    constexpr int PRE = D > 1 ? D - 1 : 1; // row pairs requested before the staging stores
+#pragma unroll
+    for (int p = 0; p < PRE; ++p) load_pair(p, p % D);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -290,8 +296,8 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
     float res[kRowsPerWaveM][MT];
 #pragma unroll
     for (int i = 0; i < kRowsPerWaveM; ++i) {
-        const int buf = i & 1;
-        if (i + 1 < kRowsPerWaveM) load_pair(i + 1, buf ^ 1);
+        const int buf = i % D;
+        if (i + D - 1 >= PRE && i + D - 1 < kRowsPerWaveM) load_pair(i + D - 1, (i + D - 1) % D);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             res[i][m] = 0.0f;
@@ -1495,7 +1501,7 @@ static hipError_t launch_w13_t(const void *x, const void *w13, const int32_t *id
         hipLaunchKernelGGL((k_w13_silu<HC, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
                            (const f16 *)x, (const f16 *)w13, ids, I, act);
     } else {
-        const int blocks = n_slots * (I / (rows_per_wave_m<SHARED>() * kWavesPerBlock));
+        const int blocks = n_slots * (I / (rows_per_wave_m<SHARED, MT>() * kWavesPerBlock));
         hipLaunchKernelGGL((k_w13_multi<HC, MT, SHARED>), dim3(blocks), dim3(kBlock), 0, s,
                            (const f16 *)x, (const f16 *)w13, M, I, K, act, table);
     }
@@ -1599,7 +1605,7 @@ static hipError_t launch_expand_m_t(const void *x, const void *w13, const void *
                                     float *act, float *s_out, const GroupTable *table, hipStream_t s)
 {
     constexpr int H = 512 * HC;
-    const int routed = n_slots * (I / (rows_per_wave_m<false>() * kWavesPerBlock));
+    const int routed = n_slots * (I / (rows_per_wave_m<false, MT>() * kWavesPerBlock));
     const int shared = Is ? H / (kWavesPerBlock * (kWave / LM::LPR)) : 0;
     hipLaunchKernelGGL((k_expand_m<HC, MT, LM>), dim3(routed + shared), dim3(kBlock), 0, s,
                        (const f16 *)x, (const f16 *)w13, (const f16 *)wsd, act_s, M, H, I, K, Is,
@@ -1626,7 +1632,7 @@ static hipError_t launch_lean_m_t(const void *x, const void *wr, const void *w13
     if constexpr (MT <= kWavesPerBlock) {
         // the selection folded into the expand launch (one wave per token)
         constexpr int H = 512 * HC;
-        const int routed = n_slots * (I / (rows_per_wave_m<false>() * kWavesPerBlock));
+        const int routed = n_slots * (I / (rows_per_wave_m<false, MT>() * kWavesPerBlock));
         return with_lane_map(lm_width, [&](auto lm) {
             using LM = decltype(lm);
             const int shared = Is ? H / (kWavesPerBlock * (kWave / LM::LPR)) : 0;

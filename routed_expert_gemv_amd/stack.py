@@ -13,7 +13,7 @@ from __future__ import annotations
 
 import torch
 
-from .api import (moe_dbg_prefill_stage, moe_decode_fused, moe_layer_decode, moe_layer_prefill,
+from .api import (moe_dbg_layer_stage, moe_dbg_prefill_stage, moe_decode_fused, moe_layer_decode, moe_layer_prefill,
                   moe_route, prefill_workspace, shared_expert, workspace)
 from .synth import LayerShape
 
@@ -22,11 +22,14 @@ class DecodeLayer:
     """Weights, inputs and preallocated outputs of one layer (all on one device).
 
     forward() runs the layer through moe_layer_decode (three launches at M = 1);
-    forward_separate() issues the three entry points one after another.
+    forward_separate() issues the three entry points one after another; with
+    single=True (M = 1 only) forward() runs the single-launch layer instead.
     """
 
-    def __init__(self, tensors: dict, shape: LayerShape, fused: bool = True):
+    def __init__(self, tensors: dict, shape: LayerShape, fused: bool = True,
+                 single: bool = False):
         self.fused = fused
+        self.single = single
         self.shape = shape
         self.t = tensors
         dev = tensors["x"].device
@@ -42,6 +45,11 @@ class DecodeLayer:
         if not self.fused:
             return self.forward_separate(stream)
         t, sh = self.t, self.shape
+        if self.single:
+            moe_dbg_layer_stage(5, t["x"], t["wr"], t["w13"], t["w2"], t["wsgu"], t["wsd"], sh.K,
+                                sh.renormalize, self.topk_ids, self.topk_w, self.logits, self.y,
+                                self.ws, stream=stream)
+            return self.y
         moe_layer_decode(t["x"], t["wr"], t["w13"], t["w2"], t["wsgu"], t["wsd"], sh.K,
                          sh.renormalize, self.topk_ids, self.topk_w, self.logits, self.y, self.ws,
                          stream=stream)
