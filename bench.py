@@ -529,15 +529,26 @@ def summarize_pmc(out_path, dirs, cmds, title):
             key = (kernel_key(name), name)
             vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     counters = sorted({c for v in vals.values() for c in v})
+    # GRBM_GUI_ACTIVE sums the GPU-busy cycles of the 8 XCDs (the 1 GiB copy
+    # kernel reads 8x the cycles of its run); TA busy cycles over the cycles of
+    # one XCD give the share of the run the memory units were busy
+    derived = "TA_BUSY_avr" in counters and "GRBM_GUI_ACTIVE" in counters
+    head = counters + (["MemUnitBusy % (TA_BUSY_avr / (GRBM_GUI_ACTIVE/8))"] if derived else [])
     lines = ["# rocprofv3 counters: " + title, ""] + ["Command: `%s`" % c for c in cmds] + [
-        "", "Average per dispatch (dispatches in parentheses).", "",
-        "| kernel | " + " | ".join(counters) + " |", "|---" * (len(counters) + 1) + "|"]
+        "", "Average per dispatch (dispatches in parentheses).  The counters are taken "
+            "with each dispatch serialised by the profiler, so kernel times here run "
+            "longer than in the graph.", "",
+        "| kernel | " + " | ".join(head) + " |", "|---" * (len(head) + 1) + "|"]
     for (k, n), v in sorted(vals.items()):
         tmpl = n[n.find("I", n.find(k) + len(k)):][:40] if "_ZN3moe" in n else ""
         cells = []
         for c in counters:
             x = v.get(c)
             cells.append("%.4g (%d)" % (sum(x) / len(x), len(x)) if x else "-")
+        if derived:
+            ta, gr = v.get("TA_BUSY_avr"), v.get("GRBM_GUI_ACTIVE")
+            cells.append("%.1f" % (100.0 * (sum(ta) / len(ta)) / (sum(gr) / len(gr) / 8))
+                         if ta and gr else "-")
         lines.append("| `%s` %s | %s |" % (k, ("`" + tmpl + "`") if tmpl else "", " | ".join(cells)))
     lines += ["", "kernel_source_sha256 (decode sources): " + sources_sha(DECODE_SRCS)]
     with open(out_path, "w") as fh:
@@ -795,6 +806,11 @@ def main():
                 "traffic": None, "avg_launch_us": round(us_layer, 3),
                 "bytes_per_launch": total_b // args.layers, "launches_timed": args.steps * args.layers,
                 "frac_method": "HIP events around the stack replays; one launch per layer"}
+        # waits that ran out over the whole run (the state block's counter,
+        # 32-bit word 1024 of each layer's workspace): 0 when every hand-off
+        # arrived in time
+        out_gave_up = sum(int(l.ws[4096:4100].view(torch.int32).item()) for l in layers)
+        roof["waits_gave_up"] = out_gave_up
     elif args.path == "fused" and sh.M == 1:
         st_us, n_launch = time_stages(layers, args.launch_reps)
         st_b = stage_bytes(sh)
