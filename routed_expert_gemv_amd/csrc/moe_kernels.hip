@@ -757,9 +757,9 @@ __global__ __launch_bounds__(kBlock) void k_expand(
     }
 }
 
-// Routed down projections and the combine, kRWaves waves per workgroup (one
-// workgroup per CU at the full-width shape).  Each wave owns RPL = 64/LPR rows
-// h, LPR lanes per row with CPL 16-byte chunks each (I = 8*LPR*CPL).  The wave
+// Routed down projections and the combine, RW = LPR/8 waves per workgroup, so
+// that a workgroup always covers 8 rows of H (H/8 workgroups: one per CU at
+// H = 2048, whatever the row width).  Each wave owns RPL = 64/LPR rows h, LPR lanes per row with CPL 16-byte chunks each (I = 8*LPR*CPL).  The wave
 // requests the ids and weights and its share of the activations [K*I], then
 // its W2 rows for up to 8/CPL experts; the workgroup stages the activations in
 // LDS while the rows arrive, then every lane accumulates as the W2 kernel
@@ -768,13 +768,14 @@ __global__ __launch_bounds__(kBlock) void k_expand(
 // SH: the shared down projection is computed here too (Is == I, so its rows
 // use the same lane mapping): s[h] = the W2 kernel's arithmetic with weight 1
 // over row h of the shared down weights and act_s, added as s_in would be.
-constexpr int kRWaves = 8;
-constexpr int kRBlock = kRWaves * kWave;
+constexpr int kRRows = 8; // rows of H per workgroup
+template <class LM>
+constexpr int reduce_waves() { return LM::LPR / 8; }
 [[maybe_unused]] constexpr int kMaxStaged = 16384; // K*I fp32 values staged in LDS (64 KB)
 
-// STAGE: 16-byte activation loads per thread, ceil(K*I / (4 * kRBlock)).
+// STAGE: 16-byte activation loads per thread, ceil(K*I / (4 * 64 * RW)).
 template <class LM, int STAGE, bool SH>
-__global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ act,
+__global__ __launch_bounds__(reduce_waves<LM>() * kWave) void k_reduce(const float *__restrict__ act,
                                                     const f16 *__restrict__ w2,
                                                     const int32_t *__restrict__ ids,
                                                     const float *__restrict__ tw,
@@ -791,6 +792,8 @@ __global__ __launch_bounds__(kRBlock) void k_reduce(const float *__restrict__ ac
     constexpr int CPL = LM::CPL;
     constexpr int RPL = kWave / LPR;
     constexpr int BATCH = 8 / CPL;
+    constexpr int kRWaves = reduce_waves<LM>();
+    constexpr int kRBlock = kRWaves * kWave;
     const int nch = I / 8;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -1436,7 +1439,7 @@ bool lean_ok(int M, int H, int E, int I, int K, int Is)
     // k_reduce stages [K*I] fp32 in LDS; its workgroups and k_expand's shared
     // workgroups cover whole row groups of H
     return M == 1 && E <= kMaxExperts && K * I <= kMaxStaged &&
-           H % (kRWaves * (kWave / lpr_of(I))) == 0 &&
+           H % kRRows == 0 &&
            (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
 }
 
@@ -1770,15 +1773,17 @@ static void launch_reduce_s(dim3 grid, size_t lds, int stage, const float *act, 
                             const int32_t *ids, const float *w, const float *s_in, const f16 *wsd,
                             const float *act_s, int H, int I, int K, f16 *y, hipStream_t s)
 {
-    const dim3 block(kRBlock);
+    const dim3 block(reduce_waves<LM>() * kWave);
     if (stage <= 1)
         hipLaunchKernelGGL((k_reduce<LM, 1, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
     else if (stage <= 2)
         hipLaunchKernelGGL((k_reduce<LM, 2, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
     else if (stage <= 4)
         hipLaunchKernelGGL((k_reduce<LM, 4, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
-    else
+    else if (stage <= 8)
         hipLaunchKernelGGL((k_reduce<LM, 8, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
+    else // K*I <= 16384 with 64 lanes per 8 rows' worth of width: at most 12 loads
+        hipLaunchKernelGGL((k_reduce<LM, 16, SH>), grid, block, lds, s, act, w2, ids, w, s_in, wsd, act_s, H, I, K, y);
 }
 
 // shared: the shared down projection runs here (wsd, act_s), else s_in (or
@@ -1788,9 +1793,12 @@ hipError_t lm_reduce(const float *act, const void *w2, const int32_t *ids, const
                      const float *s_in, const void *wsd, const float *act_s, bool shared, int H,
                      int I, int K, void *y, hipStream_t s)
 {
-    constexpr int rows = kRWaves * (kWave / LM::LPR);
+    constexpr int block = reduce_waves<LM>() * kWave;
+    constexpr int rows = reduce_waves<LM>() * (kWave / LM::LPR);
+    static_assert(rows == kRRows, "a reduce workgroup covers 8 rows");
     const size_t lds = (size_t)K * I * sizeof(float);
-    const int stage = (K * I / 4 + kRBlock - 1) / kRBlock;
+    const int stage = (K * I / 4 + block - 1) / block;
+    if (stage > 16) return hipErrorInvalidValue;
     const dim3 grid(H / rows);
     if (shared)
         launch_reduce_s<LM, true>(grid, lds, stage, act, (const f16 *)w2, ids, w, nullptr,
