@@ -138,6 +138,7 @@ def test_staged_down_kernel_at_64k_lds():
     synth.LayerShape(M=8, H=512, E=1024, K=16, I=64, Is=0),           # largest E, K, M
     synth.LayerShape(M=2, H=2048, E=8, K=2, I=2048, Is=2048),         # largest I
     synth.LayerShape(M=4, H=4096, E=16, K=4, I=1024, Is=512),         # largest H
+    synth.LayerShape(M=4, H=4096, E=256, K=16, I=2048, Is=2048),      # largest H, K, I together
     synth.LayerShape(M=2, H=2048, E=64, K=8, I=512, Is=0, renormalize=False),
 ], ids=lambda s: "M%d_H%d_E%d_K%d_I%d_Is%d_r%d" % (s.M, s.H, s.E, s.K, s.I, s.Is, s.renormalize))
 def test_edge_shapes(shape):
