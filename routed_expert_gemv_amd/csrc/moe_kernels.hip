@@ -1690,14 +1690,19 @@ template hipError_t hc_lean_m<MOE_PART>(const void *, const void *, const void *
 // ================================================================ parts 9..21: one lane mapping
 constexpr int kMaxDevices = 64;
 
-// Largest dynamic LDS a workgroup may opt into on the current device.
+// Largest dynamic LDS a workgroup may opt into on the current device (looked
+// up once per device; 64 KiB if the query fails).
 static size_t lds_optin_bytes()
 {
+    static std::atomic<int> cached[kMaxDevices] = {};
     int dev = 0, v = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess ||
+    if (hipGetDevice(&dev) != hipSuccess) return 64 * 1024;
+    if (dev >= 0 && dev < kMaxDevices && (v = cached[dev].load(std::memory_order_relaxed)) > 0)
+        return (size_t)v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess ||
         v <= 0)
         return 64 * 1024;
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store(v, std::memory_order_relaxed);
     return (size_t)v;
 }
 
