@@ -263,6 +263,13 @@ moe_status moe_probe_read(const void *src, size_t bytes, float *out, hipStream_t
  * the calibration for the memory-traffic counters. */
 moe_status moe_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
+/* The lane mapping the kernels use for down-projection rows n fp16 wide (a
+ * host query; nothing is enqueued): *lanes_per_row (LPR), *chunks_per_lane
+ * (CPL, 16-byte chunks per lane) and *padded (1 if LPR*CPL*8 > n, the steps
+ * past the row's end carrying zero weights).  Returns MOE_ERR_SHAPE unless n
+ * is a multiple of 64 in [64, 2048], MOE_ERR_NULL for a null output. */
+moe_status moe_dbg_lane_map(int n, int *lanes_per_row, int *chunks_per_lane, int *padded);
+
 /* Sums 64 fp32 values with one wavefront's cross-lane (DPP) reduction, the
  * same routine the GEMV kernels use; out[0] = the sum.  in: [64] device. */
 moe_status moe_dbg_wave_sum(const float *in, float *out, hipStream_t stream);

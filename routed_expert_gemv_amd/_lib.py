@@ -19,7 +19,7 @@ EXPORTED = ["moe_abi_version", "moe_build_id", "moe_status_str", "moe_workspace_
             "moe_dbg_w2_combine", "moe_layer_decode", "moe_layer_launches", "moe_dbg_layer_stage",
             "moe_probe_empty", "moe_probe_read", "moe_probe_copy", "moe_prefill_workspace_bytes",
             "moe_layer_prefill", "moe_dbg_prefill_stage", "moe_workspace_init",
-            "moe_layer_decode_noalloc"]
+            "moe_layer_decode_noalloc", "moe_dbg_lane_map"]
 
 _vp = C.c_void_p
 _i = C.c_int
@@ -64,6 +64,9 @@ def lib() -> C.CDLL:
                                            _vp, _vp, _sz, _vp]
             L.moe_dbg_wave_sum.restype = _i
             L.moe_dbg_wave_sum.argtypes = [_vp, _vp, _vp]
+            _ip = C.POINTER(C.c_int)
+            L.moe_dbg_lane_map.restype = _i
+            L.moe_dbg_lane_map.argtypes = [_i, _ip, _ip, _ip]
             L.moe_dbg_w13_silu.restype = _i
             L.moe_dbg_w13_silu.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]
             L.moe_dbg_w2_combine.restype = _i

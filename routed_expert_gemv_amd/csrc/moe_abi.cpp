@@ -297,6 +297,14 @@ moe_status moe_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t 
     return hip_status(launch_probe_copy(src, dst, bytes, stream));
 }
 
+moe_status moe_dbg_lane_map(int n, int *lanes_per_row, int *chunks_per_lane, int *padded)
+{
+    if (!i_ok(n)) return MOE_ERR_SHAPE;
+    if (!lanes_per_row || !chunks_per_lane || !padded) return MOE_ERR_NULL;
+    lane_map_of(n, lanes_per_row, chunks_per_lane, padded);
+    return MOE_OK;
+}
+
 moe_status moe_dbg_wave_sum(const float *in, float *out, hipStream_t stream)
 {
     if (!in || !out) return MOE_ERR_NULL;

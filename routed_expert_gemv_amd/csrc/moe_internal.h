@@ -106,6 +106,8 @@ hipError_t launch_probe_empty(hipStream_t s);
 hipError_t launch_probe_read(const void *src, size_t bytes, float *out, hipStream_t s);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream_t s);
 hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s);
+// the down-projection lane mapping of rows n fp16 wide (n % 64 == 0, 64..2048)
+void lane_map_of(int n, int *lpr, int *cpl, int *pad);
 // The layer at M = 1 in three launches (router + shared gate/up, expand, reduce);
 // stage 0 runs all three, stage 1..3 that launch alone.
 // The layer for 2..8 tokens in four launches (router + shared gate/up, the

@@ -1198,6 +1198,8 @@ using LaneMaps = TypeList<LaneMap<8, 1, false>, LaneMap<16, 1, false>, LaneMap<8
 // f(LaneMap) with the lane mapping of rows n fp16 wide (n % 64 == 0, 64 <= n
 // <= 2048, as the entry points require): exact where n/8 = LPR*CPL, LPR in
 // {8, 16, 32, 64}, CPL <= 4 (largest LPR), padded 64-lane rows otherwise.
+// n = 1536 (64 lanes x 3 chunks) runs on the padded 64 x 3 instance, whose
+// steps then all lie inside the row: the same arithmetic as an exact one.
 template <class F>
 static auto with_lane_map(int n, F &&f) -> decltype(f(NoLaneMap{}))
 {
@@ -1426,6 +1428,19 @@ hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes, hipStream
     hipLaunchKernelGGL(k_probe_copy, dim3(blocks), dim3(256), 0, s, (const f16x8 *)src,
                        (f16x8 *)dst, n16);
     return last();
+}
+
+void lane_map_of(int n, int *lpr, int *cpl, int *pad)
+{
+    with_lane_map(n, [&](auto lm) {
+        using LM = decltype(lm);
+        *lpr = LM::LPR;
+        *cpl = LM::CPL;
+        // padded when a step lies past the row's end (n = 1536 runs the
+        // padded instance, whose steps all lie inside the row)
+        *pad = LM::LPR * LM::CPL * 8 > n ? 1 : 0;
+        return 0;
+    });
 }
 
 hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s)

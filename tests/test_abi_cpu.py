@@ -141,6 +141,36 @@ def test_decode_boundary_accept_and_reject_sets():
             assert shared(Is=I) == layer(I=512, Is=I) == -2, I
 
 
+def test_lane_map_rule():
+    """The down-projection lane mapping of every accepted width: exact where
+    n/8 = LPR*CPL with LPR in {8, 16, 32, 64} and CPL <= 4 (the largest such
+    LPR), else 64 lanes and ceil(n/512) chunks with the steps past the row
+    padded; and the widths named in the header."""
+    L = _lib.lib()
+
+    def lm(n):
+        a, b, c = C.c_int(), C.c_int(), C.c_int()
+        st = L.moe_dbg_lane_map(n, C.byref(a), C.byref(b), C.byref(c))
+        return st, a.value, b.value, c.value
+
+    for n in I_ACCEPT:
+        st, lpr, cpl, pad = lm(n)
+        assert st == 0
+        chunks = n // 8
+        exact = [l for l in (64, 32, 16, 8) if chunks % l == 0 and chunks // l <= 4]
+        if exact:
+            assert (lpr, cpl, pad) == (exact[0], chunks // exact[0], 0), n
+        else:
+            assert (lpr, cpl, pad) == (64, -(-chunks // 64), 1), n
+        assert lpr * cpl * 8 >= n and lpr * (cpl - 1) * 8 < n   # no wholly empty step
+    assert lm(768)[1:] == (32, 3, 0) and lm(192)[1:] == (8, 3, 0) and lm(384)[1:] == (16, 3, 0)
+    assert lm(512)[1:] == (64, 1, 0) and lm(2048)[1:] == (64, 4, 0) and lm(128)[1:] == (16, 1, 0)
+    assert lm(320)[1:] == (64, 1, 1) and lm(1536)[1:] == (64, 3, 0) and lm(1984)[1:] == (64, 4, 1)
+    for n in I_REJECT:
+        assert lm(n)[0] == -2
+    assert L.moe_dbg_lane_map(512, None, None, None) == -1
+
+
 def test_route_validation():
     L = _lib.lib()
     ok = dict(M=1, H=2048, E=256, K=8)
