@@ -54,6 +54,16 @@ def moe_abi_version() -> int:
     return int(_lib.lib().moe_abi_version())
 
 
+def moe_status_str(status: int) -> str:
+    """The library's name for a status code."""
+    return _lib.lib().moe_status_str(int(status)).decode()
+
+
+def moe_build_id() -> str:
+    """SHA-256 of the sources the loaded library was built from."""
+    return _lib.lib().moe_build_id().decode()
+
+
 def moe_workspace_bytes(M: int, H: int, E: int, I: int, K: int, Is: int = 0) -> int:
     return int(_lib.lib().moe_workspace_bytes(M, H, E, I, K, Is))
 
@@ -155,6 +165,17 @@ def moe_decode_fused(x, w13, w2, topk_ids, topk_w, shared_in=None, y=None, ws=No
                                      _stream(stream, dev))
     _check("moe_decode_fused", st)
     return y
+
+
+def moe_dbg_lane_map(n: int):
+    """The lane mapping of down-projection rows n fp16 wide (host query):
+    (lanes per row, 16-byte chunks per lane, whether steps past the row are
+    padded)."""
+    import ctypes as C
+    a, b, c = C.c_int(), C.c_int(), C.c_int()
+    _check("moe_dbg_lane_map", _lib.lib().moe_dbg_lane_map(int(n), C.byref(a), C.byref(b),
+                                                          C.byref(c)))
+    return a.value, b.value, bool(c.value)
 
 
 def moe_dbg_wave_sum(values, out=None, stream=None):

@@ -61,6 +61,9 @@ def test_every_declared_symbol_is_exported():
     for n in names:
         assert hasattr(L, n), "declared symbol %s is not exported" % n
     assert set(names) == set(_lib.EXPORTED)
+    # the Python binding carries the same names
+    import routed_expert_gemv_amd as m
+    assert [n for n in names if not hasattr(m, n)] == []
 
 
 def test_abi_version_matches_header():
