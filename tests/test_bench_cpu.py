@@ -36,3 +36,59 @@ def test_committed_counters_use_the_same_accounting():
         assert v["algorithmic_bytes_per_dispatch"] == st[k]
     # calibrated HBM bytes within a few percent of the algorithmic bytes: no re-reads
     assert abs(c["hbm_bytes_per_dispatch"] / st["k_expand"] - 1) < 0.03
+
+
+def test_committed_traces_and_counters_of_both_single_token_shapes():
+    """The committed kernel-trace summaries carry the stage-graph averages that
+    bench.py reads, for the kernels it times, and the C2 counter summary uses
+    the same byte accounting as the bench."""
+    for shape in ("full_e256_k8_i512", "tp4_shard_e256_k8_i128"):
+        text = open(bench.trace_path(shape)).read()
+        blob = json.loads(text.rsplit("```json", 1)[1].split("```", 1)[0])
+        assert set(blob["stage_avg_us"]) == set(bench.STAGES), shape
+        assert all(0 < v < 100 for v in blob["stage_avg_us"].values())
+        assert len(blob["kernel_source_sha256"]) == 64
+        c = json.load(open(bench.counters_path(shape)))
+        st = bench.stage_bytes(synth.SHAPES[shape])
+        assert c["algorithmic_bytes_per_dispatch"] == st["k_expand"], shape
+        assert abs(c["hbm_bytes_per_dispatch"] / st["k_expand"] - 1) < 0.03, shape
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_trace_summary_finds_stage_graph_dispatches(tmp_path):
+    """Dispatches whose neighbours are the same kernel are the stage graphs'."""
+    d = tmp_path / "tr"
+    names = ["_ZN3moe9k_router1ILi4EEEvPKDF16_S2_Pf", "_ZN3moe8k_expandILi4E", "_ZN3moe8k_reduceIN"]
+    rows, t = [], 0
+    for n in names * 2:                    # two full layers
+        rows.append([t, t + 1000, n]); t += 2000
+    for n, dur in zip(names, (2000, 7000, 4000)):   # a stage graph of 4 launches each
+        for _ in range(4):
+            rows.append([t, t + dur, n]); t += dur + 100
+    _write_csv(str(d / "x" / "tr_kernel_trace.csv"), ["Start_Timestamp", "End_Timestamp", "Kernel_Name"], rows)
+    out = tmp_path / "s.md"
+    bench.summarize_trace(str(d), str(out), "cmd")
+    blob = json.loads(out.read_text().rsplit("```json", 1)[1].split("```", 1)[0])
+    assert blob["stage_avg_us"] == {"k_router1": 2.0, "k_expand": 7.0, "k_reduce": 4.0}
+
+
+def test_pmc_summary_derives_memory_unit_busy(tmp_path):
+    d = tmp_path / "p"
+    rows = [["_ZN3moe8k_expandILi4E", "TA_BUSY_avr", 100.0], ["_ZN3moe8k_expandILi4E", "GRBM_GUI_ACTIVE", 8000.0],
+            ["_ZN3moe8k_expandILi4E", "TA_BUSY_avr", 300.0], ["_ZN3moe8k_expandILi4E", "GRBM_GUI_ACTIVE", 8000.0],
+            ["at::native::other", "TA_BUSY_avr", 5.0]]
+    _write_csv(str(d / "x" / "pmc_counter_collection.csv"), ["Kernel_Name", "Counter_Name", "Counter_Value"], rows)
+    out = tmp_path / "c.md"
+    bench.summarize_pmc(str(out), [str(d)], ["cmd"], "t")
+    line = [l for l in out.read_text().splitlines() if l.startswith("| `k_expand`")][0]
+    # TA busy 200 cycles on average over one XCD's 1000 cycles
+    assert line.rstrip(" |").endswith("20.0")
+    assert "at::native" not in out.read_text()
