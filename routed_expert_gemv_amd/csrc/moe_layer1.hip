@@ -22,8 +22,9 @@
 //   * each workgroup then selects the experts itself (only as many top-k
 //     rounds as its own gate/up rows need before it requests them);
 //   * gate/up: one row pair per wave (K*I pairs over 4096 waves), SiLU*mul in
-//     registers; the shared expert's gate/up rows and every down row the
-//     workgroup will need are requested before any routing is known;
+//     registers; the shared expert's gate/up and down rows are requested
+//     before any routing is known, and the routed down rows as soon as the
+//     workgroup has all K expert ids, before the activation hand-off;
 //   * the activations cross the XCDs once: write-through (sc1) stores, one
 //     flag per workgroup, sc1 polls; the W2 rows are already in flight, so the
 //     hand-off overlaps the W2 stream;
