@@ -46,6 +46,10 @@ HBM_PEAK_GBS = 8000.0
 LAYERS = 36
 COUNTERS = os.path.join(ROOT, "profiles", "k_expand_counters_full_e256_k8_i512.json")
 STAGES = ("k_router1", "k_expand", "k_reduce")
+# the three steps of a layer of 2..8 tokens (the selection launch and the
+# expand launch count as one step at M = 5..8)
+STAGES_M = ("k_route_shared_m", "k_expand_sel_m", "k_w2_staged")
+STAGES_M8 = ("k_route_shared_m", "k_select_m+k_expand_m", "k_w2_staged")
 KERNEL_SRC = os.path.join(ROOT, "routed_expert_gemv_amd", "csrc", "moe_kernels.hip")
 # sources the decode kernels are compiled from (a summary taken on other
 # sources no longer describes the kernels that run)
@@ -88,6 +92,24 @@ def stage_bytes(sh):
     expand = 2 * K * 2 * I * H + 2 * 2 * Is * H + 2 * H + 4 * E + 4 * K * I + 4 * Is + 8 * K
     reduce = 2 * K * H * I + 2 * H * Is + 4 * K * I + 4 * Is + 8 * K + 2 * H
     return dict(zip(STAGES, (router, expand, reduce)))
+
+
+def stage_bytes_m(sh, n_distinct):
+    """Algorithmic bytes of the three steps of a layer of M = sh.M > 1 tokens
+    with n_distinct distinct experts and a shared expert as wide as a routed
+    one, or none: router rows and shared gate/up rows; the distinct experts'
+    gate/up rows and the shared down rows; their down rows.  Weights read once,
+    x once, and the small tensors each step reads or writes (logits, routing
+    ids/weights, routed and shared activations, shared output, y)."""
+    M, H, E, K, I, Is = sh.M, sh.H, sh.E, sh.K, sh.I, sh.Is
+    assert Is in (0, I), "stage bytes are for the benched shared-expert width"
+    route = 2 * E * H + 2 * 2 * Is * H + 2 * M * H + 4 * M * E + 4 * M * Is
+    expand = (2 * 2 * n_distinct * I * H + 2 * H * Is + 2 * M * H + 4 * M * E + 8 * M * K
+              + 4 * M * K * I + 4 * M * Is + (4 * M * H if Is else 0))
+    w2 = (2 * n_distinct * H * I + 4 * M * K * I + 8 * M * K + (4 * M * H if Is else 0)
+          + 2 * M * H)
+    names = STAGES_M if M <= 4 else STAGES_M8
+    return dict(zip(names, (route, expand, w2)))
 
 
 def prefill_stage_bytes(sh, n_distinct):
@@ -230,11 +252,12 @@ def replay_percentiles(stack, n, layers):
     return [pick(0.1), pick(0.5), pick(0.9)]
 
 
-def time_stages(layers, reps):
-    """Average duration of each of the three kernels of a layer: for each kernel,
-    a hipGraph of that kernel alone for every layer of the stack (inputs left
-    by the full calls before it; the layers rotate, so weights stream cold),
-    replayed `reps` times between two HIP events on the replay stream."""
+def time_stages(layers, reps, names=STAGES):
+    """Average duration of each of the three steps of a layer (at M = 1 one
+    kernel each): for each step, a hipGraph of that step alone for every layer
+    of the stack (inputs left by the full calls before it; the layers rotate,
+    so weights stream cold), replayed `reps` times between two HIP events on
+    the replay stream."""
     import torch
     import routed_expert_gemv_amd as moe
 
@@ -248,7 +271,7 @@ def time_stages(layers, reps):
         layer.forward()
     torch.cuda.synchronize()
     us = {}
-    for i, name in enumerate(STAGES):
+    for i, name in enumerate(names):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for layer in layers:
@@ -834,6 +857,26 @@ def main():
             roof["rocprof_avg_launch_us"] = rp[dom]
             roof["rocprof_frac"] = round(st_b[dom] / (rp[dom] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
             roof["rocprof_summary"] = os.path.relpath(trace_path(args.shape), ROOT)
+
+    elif args.path == "fused":
+        names = STAGES_M if sh.M <= 4 else STAGES_M8
+        st_us, n_launch = time_stages(layers, args.launch_reps, names)
+        nd_avg = sum(n_distinct) / len(n_distinct)
+        st_b = {k: int(round(v)) for k, v in stage_bytes_m(sh, nd_avg).items()}
+        dom = max(names, key=lambda k: st_us[k])
+        k_gbs = st_b[dom] / (st_us[dom] * 1e-6) / 1e9
+        log("steps (HIP events over stage graphs, %d each): %s" % (n_launch, ", ".join(
+            "%s %.2f us %.0f GB/s" % (k, st_us[k], st_b[k] / (st_us[k] * 1e-6) / 1e9)
+            for k in names)))
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(k_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                "traffic": None, "avg_launch_us": round(st_us[dom], 3),
+                "bytes_per_launch": st_b[dom], "launches_timed": n_launch,
+                "frac_method": "HIP events around %d replays of a graph of the step alone for "
+                               "every layer, divided by the launches; bytes at the stack's mean "
+                               "distinct experts per layer" % args.launch_reps,
+                "per_kernel_us": {k: round(v, 3) for k, v in st_us.items()},
+                "per_kernel_bytes": st_b}
 
     out = {
         "metric": METRIC, "value": round(gbs_expert, 1), "unit": "GB/s",

@@ -214,14 +214,21 @@ int moe_layer_launches(int M, int H, int E, int I, int K, int Is);
 
 /* ---- test-only probes (not part of the decode path) --------------------- */
 
-/* moe_layer_decode at M = 1 by a chosen path, for tests and timing.
- * Stages 1..3 run one launch of the three-launch path alone: 1 = router
- * (writes logits; with Is != I also the shared activations, to ws), 2 = expand
- * (reads them; writes topk_ids, topk_w, the routed activations, and the shared
- * activations (Is == I) or the shared output (Is != I)), 3 = reduce (reads
- * those; writes y).  A stage reads what the previous stage left in the same
- * buffers, so only a full call (or stages 1, 2, 3 in order) on them makes its
- * inputs valid.  Stage 4 runs the three-launch path whole.
+/* moe_layer_decode by a chosen path, for tests and timing.
+ * Stages 1..3 run one step of moe_layer_decode's launches alone.  At M = 1:
+ * 1 = router (writes logits; with Is != I also the shared activations, to
+ * ws), 2 = expand (reads them; writes topk_ids, topk_w, the routed
+ * activations, and the shared activations (Is == I) or the shared output
+ * (Is != I)), 3 = reduce (reads those; writes y).  At M = 2..8: 1 = router and
+ * shared gate/up rows (logits, shared activations), 2 = the selection and the
+ * distinct experts' gate/up rows with the shared down rows (one launch at
+ * M <= 4, two at M = 5..8; topk_ids, topk_w, the group table, the routed
+ * activations, the shared output), 3 = the down rows and the combine (y).  A
+ * stage reads what the previous stage left in the same buffers, so only a
+ * full call (or stages 1, 2, 3 in order) on them makes its inputs valid.
+ * Stage 4 runs the launches whole (moe_layer_decode).  Sizes that
+ * moe_layer_decode runs as the separate calls' kernels (see
+ * moe_layer_launches) take no stage 1..4.
  *
  * Stage 5 runs the layer as ONE launch, on a GPU with 256 CUs in 8 XCDs
  * (MI355X), for H in {1024, 2048}, E <= 256, K <= 8, I in {64, ..., 1024},

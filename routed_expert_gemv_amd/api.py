@@ -305,13 +305,14 @@ def moe_layer_decode_noalloc(x, w_router, w13, w2, w_gate_up=None, w_down=None, 
 def moe_dbg_layer_stage(stage: int, x, w_router, w13, w2, w_gate_up=None, w_down=None,
                         K: int = 8, renormalize: bool = True, topk_ids=None, topk_w=None,
                         logits=None, y=None, ws=None, stream=None):
-    """Test and benchmark probe of moe_layer_decode at M = 1.  Stage 1, 2, 3:
-    one launch of the three-launch path (router; expand; reduce -- the shared
-    expert's rows go with them as that path places them), alone, on buffers a
-    full call already filled; 4: the three-launch path whole; 5: the
-    single-launch path; 6: the single-launch path with every wait giving up at
-    once (each workgroup computes what it would have waited for).
-    Returns (y, topk_ids, topk_w, logits)."""
+    """Test and benchmark probe of moe_layer_decode.  Stage 1, 2, 3: one step
+    of the layer's launches (router; selection and gate/up rows; down rows
+    and combine -- the shared expert's rows go with them as the layer places
+    them; one launch each, except the selection launch of M = 5..8), alone,
+    on buffers a full call already filled; 4: the layer's launches whole; 5
+    (M = 1): the single-launch path; 6: the single-launch path with every
+    wait giving up at once (each workgroup computes what it would have waited
+    for).  Returns (y, topk_ids, topk_w, logits)."""
     out, args = _layer_call(x, w_router, w13, w2, w_gate_up, w_down, K, renormalize, topk_ids,
                             topk_w, logits, y, ws)
     st = _lib.lib().moe_dbg_layer_stage(int(stage), *args, _stream(stream, x.device))

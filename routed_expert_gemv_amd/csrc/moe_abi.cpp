@@ -86,11 +86,13 @@ static moe_status layer_decode(const void *x, const void *w_router, const void *
         (shared && (!al(w_gate_up, 16) || !al(w_down, 16))))
         return MOE_ERR_ALIGN;
     if (ws_bytes < routed_ws_bytes(M, I, K)) return MOE_ERR_WORKSPACE;
-    // stage 1..3: one launch of the three-launch path; stage 4: the three-launch
-    // path whole; 5: the single launch; 6: the single launch with every wait
-    // giving up at once
+    // stage 1..3: one step of the layer launches (M = 1: one launch each; M > 1:
+    // router, selection with gate/up, W2); stage 4: the layer launches whole;
+    // 5: the single launch; 6: the single launch with every wait giving up at
+    // once
     if (stage < 0 || stage > 6) return MOE_ERR_SHAPE;
-    if (stage >= 1 && stage <= 4 && !lean_ok(M, H, E, I, K, Is)) return MOE_ERR_SHAPE;
+    if (stage >= 1 && stage <= 4 && !lean_ok(M, H, E, I, K, Is) && !lean_m_ok(M, H, E, I, K, Is))
+        return MOE_ERR_SHAPE;
     if (stage >= 5 && !layer1_ok(M, H, E, I, K, Is)) return MOE_ERR_SHAPE;
     char *base = static_cast<char *>(ws);
     float *act_s = reinterpret_cast<float *>(base + kScratch);
@@ -107,11 +109,11 @@ static moe_status layer_decode(const void *x, const void *w_router, const void *
                                       stream));
     float *s_out = shared ? reinterpret_cast<float *>(base + kSharedOutOffset) : nullptr;
     GroupTable *table = reinterpret_cast<GroupTable *>(base + kGroupOffset);
-    if (stage == 0 && lean_m_ok(M, H, E, I, K, Is))
+    if (lean_m_ok(M, H, E, I, K, Is))
         return hip_status(launch_lean_m(x, w_router, w13, w2, w_gate_up, w_down, M, H, E, I, K,
                                         Is, renormalize, topk_ids, topk_w, logits, y, act, act_s,
                                         reinterpret_cast<float *>(base + kSharedOutOffset),
-                                        table, stream));
+                                        table, stage, stream));
     hipError_t err = hipSuccess;
     if (shared) err = launch_shared(x, w_gate_up, w_down, M, H, Is, s_out, act_s, stream);
     if (err == hipSuccess)

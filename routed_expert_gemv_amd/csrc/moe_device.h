@@ -18,6 +18,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 // Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of the buffer-load builtins: nontemporal (the weight
+// streams are read once, as the global loads' __builtin_nontemporal_load).
+constexpr int kLoadNT = 2;
 
 // ---------------------------------------------------------------- helpers
 __device__ __forceinline__ f16x8 stream_load(const f16x8 *p)
@@ -230,6 +233,26 @@ __device__ __forceinline__ void wave_topk_keys(uint32_t (&key)[N], int (&id)[N],
     my_key = 0u;
     my_id = 0;
     topk_rounds<N>(key, id, 0, K, my_key, my_id);
+}
+
+// Place of expert e in the top-k order of the wave's (key, id) pairs (key 0 =
+// no entry; keys of real entries are nonzero): how many pairs have a larger
+// key, or an equal key and a lower id.  The selection takes e iff that is
+// below K, and e is then its rank-th choice.  e must be one of the pairs
+// (the entry of id e, wherever the pairs were moved within their lane); the
+// result is wave-uniform.
+template <int N>
+__device__ __forceinline__ int topk_rank(const uint32_t (&key)[N], const int (&id)[N], int e)
+{
+    uint32_t ke = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ke = id[i] == e ? key[i] : ke;
+    ke = wave_max_u32(ke); // the one lane holding e supplies its key
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        r += __builtin_popcountll(__ballot(key[i] > ke || (key[i] == ke && id[i] < e)));
+    return r;
 }
 
 // The (key, id) pairs of E <= 64*NPL logits held by the wave (v[i] is the

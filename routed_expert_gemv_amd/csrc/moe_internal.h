@@ -110,13 +110,16 @@ hipError_t launch_dbg_wave_sum(const float *in, float *out, hipStream_t s);
 void lane_map_of(int n, int *lpr, int *cpl, int *pad);
 // The layer at M = 1 in three launches (router + shared gate/up, expand, reduce);
 // stage 0 runs all three, stage 1..3 that launch alone.
-// The layer for 2..8 tokens in four launches (router + shared gate/up, the
-// selection with the group table, expand, the staged W2 kernel).
+// The layer for 2..8 tokens: router + shared gate/up; the selection with the
+// gate/up rows (one launch at M <= 4; a selection launch and the expand
+// launch at M = 5..8); the staged W2 kernel.  stage 0 runs every launch,
+// stage 1..3 one of those three steps alone.
 bool lean_m_ok(int M, int H, int E, int I, int K, int Is);
 hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const void *w2,
                          const void *wsgu, const void *wsd, int M, int H, int E, int I, int K,
                          int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
-                         float *act, float *act_s, float *s_out, GroupTable *table, hipStream_t s);
+                         float *act, float *act_s, float *s_out, GroupTable *table, int stage,
+                         hipStream_t s);
 bool lean_ok(int M, int H, int E, int I, int K, int Is);
 // The layer at M = 1 in one launch (moe_layer1.hip); spin bounds each wait
 // (0: every wait gives up at once and computes the data itself).

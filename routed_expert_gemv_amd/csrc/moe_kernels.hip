@@ -219,13 +219,16 @@ __global__ __launch_bounds__(kBlock) void k_w13_silu(const f16 *__restrict__ x,
 template <bool SHARED, int MT>
 constexpr int rows_per_wave_m() { return SHARED ? 1 : MT == 4 ? 4 : 2; }
 
-// Workgroup b of the multi-token W13 work (xs: LDS for x, MT*HC*64 chunks).
-template <int HC, int MT, bool SHARED>
-__device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
-                                                const f16 *__restrict__ w13, int M, int I, int K,
-                                                float *__restrict__ act,
-                                                const GroupTable *__restrict__ table, int b,
-                                                f16x8 *xs)
+// Workgroup b's row pairs of `expert` (xs: LDS for x, MT*HC*64 chunks).  The
+// row pairs and x are requested first; then mid(mask, slot) gives the tokens
+// routed to the expert and their slots (it may hold barriers: every thread of
+// the workgroup calls it), so that they can still be worked out while the
+// rows are in flight; then x is staged and the products computed.
+template <int HC, int MT, bool SHARED, class Mid>
+__device__ __forceinline__ void w13_multi_rows(const f16 *__restrict__ x,
+                                               const f16 *__restrict__ w13, int M, int I, int K,
+                                               float *__restrict__ act, int expert, int b,
+                                               f16x8 *xs, Mid &&mid)
 {
     constexpr int H = 512 * HC;
     constexpr int kRowsPerWaveM = rows_per_wave_m<SHARED, MT>();
@@ -233,24 +236,7 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int bpe = I / kRowsPerBlockM;
-    const int u = b / bpe;
     const int j0 = (b % bpe) * kRowsPerBlockM + wave;
-
-    int expert;
-    unsigned mask;
-    int slot[MT];
-    if (SHARED) {
-        expert = 0;
-        mask = (1u << M) - 1u;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) slot[m] = 0;
-    } else {
-        if (u >= table->n_u) return; // fewer distinct experts than slots: nothing to do
-        expert = table->u_expert[u];
-        mask = table->u_mask[u];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) slot[m] = table_slot(table, u, m);
-    }
     const f16 *base = w13 + (size_t)expert * 2 * I * H;
     constexpr int D = kRowsPerWaveM < 2 ? kRowsPerWaveM : 2; // row pairs in flight
     f16x8 wg[D][HC], wu[D][HC];
@@ -282,6 +268,9 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
 #pragma unroll
     for (int p = 0; p < PRE; ++p) load_pair(p, p % D);
     __builtin_amdgcn_sched_barrier(0);
+    unsigned mask;
+    int slot[MT];
+    mid(mask, slot);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int q = threadIdx.x + i * kBlock;
@@ -319,6 +308,40 @@ __device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
                 if (mask & (1u << m))
                     act[((size_t)m * K + slot[m]) * I + j0 + i * kWavesPerBlock] = res[i][m];
     }
+}
+
+// Workgroup b of the multi-token W13 work: distinct expert u = b / (blocks
+// per expert) of the group table (SHARED: the shared expert, every token).
+template <int HC, int MT, bool SHARED>
+__device__ __forceinline__ void w13_multi_block(const f16 *__restrict__ x,
+                                                const f16 *__restrict__ w13, int M, int I, int K,
+                                                float *__restrict__ act,
+                                                const GroupTable *__restrict__ table, int b,
+                                                f16x8 *xs)
+{
+    constexpr int kRowsPerBlockM = rows_per_wave_m<SHARED, MT>() * kWavesPerBlock;
+    const int u = b / (I / kRowsPerBlockM);
+    int expert;
+    unsigned mask;
+    int slot[MT];
+    if (SHARED) {
+        expert = 0;
+        mask = (1u << M) - 1u;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) slot[m] = 0;
+    } else {
+        if (u >= table->n_u) return; // fewer distinct experts than slots: nothing to do
+        expert = table->u_expert[u];
+        mask = table->u_mask[u];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) slot[m] = table_slot(table, u, m);
+    }
+    w13_multi_rows<HC, MT, SHARED>(x, w13, M, I, K, act, expert, b, xs,
+                                   [&](unsigned &mk, int (&sl)[MT]) {
+                                       mk = mask;
+#pragma unroll
+                                       for (int m = 0; m < MT; ++m) sl[m] = slot[m];
+                                   });
 }
 
 template <int HC, int MT, bool SHARED>
@@ -481,7 +504,7 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
                 wv[buf][t][c] = lm_weights<LM>(
                     __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                                   rs, (uint32_t)(h * I + lm_chunk<LM>(c, cl, nch) * 8) * 2,
-                                                  0, 0)),
+                                                  0, kLoadNT)),
                     c, cl, nch);
         }
     };
@@ -1054,12 +1077,20 @@ __global__ __launch_bounds__(kBlock) void k_expand_m(const f16 *__restrict__ x,
 }
 
 // k_expand_m with the selection folded in (M <= 4, one wave per token): every
-// routed workgroup selects each token's experts (the top-k kernel's
-// arithmetic) and builds the group table in LDS itself, so the separate
-// selection launch and its hand-off are gone; workgroup 0 also writes ids,
-// weights and the table that the W2 kernel reads.  The shared workgroups are
-// k_expand_m's.  (At M = 8 each wave would select for two tokens in turn, and
-// the selection launch is kept.)
+// routed workgroup selects its expert itself, so the separate selection
+// launch and its hand-off are gone.  The group table lists token 0's experts
+// first, in routing order, so distinct expert u < K is token 0's u-th choice:
+// its workgroups run u + 1 top-k rounds on token 0 (the top-k kernel's
+// rounds), request their row pairs at once, and while the rows are in flight
+// find every other token's place of that expert in its own top-k order
+// (topk_rank), which gives the token mask and slots of the group table's
+// entry u.  The workgroups of a later entry run every token's selection and
+// build the group table in LDS (the same device functions as k_select_m)
+// before they request their rows.  Workgroup 0 (entry 0) also runs the full
+// selection while its rows are in flight and, after its products, writes
+// ids, weights and the table that the W2 kernel reads.  The shared
+// workgroups are k_expand_m's.  (At M = 8 each wave would select for two
+// tokens in turn, and the selection launch is kept.)
 template <int HC, int MT, class LM, int NPL>
 __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
     const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsd,
@@ -1068,46 +1099,99 @@ __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
     float *__restrict__ weights, float *__restrict__ act, float *__restrict__ s_out,
     GroupTable *__restrict__ table)
 {
+    static_assert(MT <= kWavesPerBlock, "one wave per token");
     __shared__ f16x8 xs[MT * HC * kWave];
     __shared__ GroupScratch g;
     __shared__ GroupTable tl;
     __shared__ int32_t sids[kMaxSlots];
+    __shared__ int s_e;
+    __shared__ int s_rank[MT];
     const int b = blockIdx.x;
     const int lane = lane_id();
-    if (b < routed_blocks) {
-        const int wave = threadIdx.x / kWave;
-        const bool writer = b == 0;
-        for (int m = wave; m < M; m += kWavesPerBlock) {
-            const float *L = logits + (size_t)m * E;
-            float v[NPL];
+    if (b >= routed_blocks) {
+        shared_down_rows<LM, MT>(wsd, act_s, M, H, Is,
+                                 (b - routed_blocks) * kWavesPerBlock + threadIdx.x / kWave, s_out);
+        return;
+    }
+    const int wave = threadIdx.x / kWave;
+    constexpr int kRowsPerBlockM = rows_per_wave_m<false, MT>() * kWavesPerBlock;
+    const int u = b / (I / kRowsPerBlockM);
+    // wave m < M: token m's logits and (key, id) pairs
+    const bool tok = wave < M;
+    float v[NPL];
+    uint32_t key[NPL];
+    int id[NPL];
+    {
+        const float *L = logits + (size_t)(tok ? wave : 0) * E;
 #pragma unroll
-            for (int i = 0; i < NPL; ++i) v[i] = i * kWave + lane < E ? L[i * kWave + lane] : 0.0f;
+        for (int i = 0; i < NPL; ++i) v[i] = i * kWave + lane < E ? L[i * kWave + lane] : 0.0f;
+        topk_pairs<NPL>(v, E, key, id);
+    }
+    if (u >= K) {
+        // a later entry: every token's selection, then the group table
+        if (tok) {
+            uint32_t my_key;
             int my_id;
-            float my_l;
-            const float lmax = wave_topk_vals<NPL>(v, E, K, my_id, my_l);
-            if (lane < K) sids[m * K + lane] = my_id;
-            if (writer) {
-                const float w = topk_weight_vals<NPL>(v, E, K, renormalize, my_l, lmax);
-                if (lane < K) {
-                    ids[(size_t)m * K + lane] = my_id;
-                    weights[(size_t)m * K + lane] = w;
-                }
-            }
+            wave_topk_keys<NPL>(key, id, K, my_key, my_id);
+            if (lane < K) sids[wave * K + lane] = my_id;
         }
         __syncthreads();
         build_group_table(sids, M, K, E, &tl, g);
         __syncthreads();
-        if (writer) {
-            const int *src = reinterpret_cast<const int *>(&tl);
-            int *dst = reinterpret_cast<int *>(table);
-            for (int i = threadIdx.x; i < (int)(sizeof(GroupTable) / sizeof(int)); i += kBlock)
-                dst[i] = src[i];
-        }
         w13_multi_block<HC, MT, false>(x, w13, M, I, K, act, &tl, b, xs);
         return;
     }
-    shared_down_rows<LM, MT>(wsd, act_s, M, H, Is,
-                             (b - routed_blocks) * kWavesPerBlock + threadIdx.x / kWave, s_out);
+    // token 0's u-th choice
+    const bool writer = b == 0;
+    uint32_t my_key = 0u;
+    int my_id = 0;
+    if (wave == 0) {
+        topk_sort_lane<NPL>(key, id);
+        topk_rounds<NPL>(key, id, 0, u + 1, my_key, my_id);
+        if (lane == u) s_e = my_id;
+    }
+    __syncthreads();
+    const int e = s_e;
+    float w = 0.0f;
+    w13_multi_rows<HC, MT, false>(x, w13, M, I, K, act, e, b, xs, [&](unsigned &mask, int (&slot)[MT]) {
+        if (wave > 0 && tok) {
+            const int r = topk_rank<NPL>(key, id, e);
+            if (lane == 0) s_rank[wave] = r;
+        }
+        if (writer) {
+            // the full selection (token 0 continues from round u + 1) and the
+            // group table, kept in LDS and registers until the products are done
+            if (tok) {
+                if (wave > 0) topk_sort_lane<NPL>(key, id);
+                topk_rounds<NPL>(key, id, wave > 0 ? 0 : u + 1, K, my_key, my_id);
+                const float my_l = my_key ? key_value(my_key) : 0.0f;
+                const float lmax = key_value((uint32_t)__builtin_amdgcn_readlane((int)my_key, 0));
+                w = topk_weight_vals<NPL>(v, E, K, renormalize, my_l, lmax);
+                if (lane < K) sids[wave * K + lane] = my_id;
+            }
+            __syncthreads();
+            build_group_table(sids, M, K, E, &tl, g);
+        }
+        __syncthreads();
+        mask = 1u;
+        slot[0] = u;
+#pragma unroll
+        for (int m = 1; m < MT; ++m) {
+            const int r = m < M ? s_rank[m] : K;
+            if (r < K) mask |= 1u << m;
+            slot[m] = r < K ? r : 0;
+        }
+    });
+    if (writer) {
+        if (tok && lane < K) {
+            ids[(size_t)wave * K + lane] = my_id;
+            weights[(size_t)wave * K + lane] = w;
+        }
+        const int *src = reinterpret_cast<const int *>(&tl);
+        int *dst = reinterpret_cast<int *>(table);
+        for (int i = threadIdx.x; i < (int)(sizeof(GroupTable) / sizeof(int)); i += kBlock)
+            dst[i] = src[i];
+    }
 }
 
 // ---------------------------------------------------------------- probes
@@ -1269,7 +1353,7 @@ template <int HC>
 hipError_t hc_lean_m(const void *x, const void *wr, const void *w13, const void *wsgu,
                      const void *wsd, int M, int E, int I, int K, int Is, int renorm,
                      int32_t *ids, float *w, float *logits, float *act, float *act_s,
-                     float *s_out, GroupTable *table, hipStream_t s);
+                     float *s_out, GroupTable *table, int stage, hipStream_t s);
 // ---- per-lane-mapping entry points (defined in the part of that mapping)
 template <class LM>
 hipError_t lm_w2(bool shared, const float *act, const void *w2, const int32_t *ids,
@@ -1469,13 +1553,20 @@ bool lean_m_ok(int M, int H, int E, int I, int K, int Is)
 hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const void *w2,
                          const void *wsgu, const void *wsd, int M, int H, int E, int I, int K,
                          int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
-                         float *act, float *act_s, float *s_out, GroupTable *table, hipStream_t s)
+                         float *act, float *act_s, float *s_out, GroupTable *table, int stage,
+                         hipStream_t s)
 {
-    const hipError_t err = with_hc(H, [&](auto hc) {
-        return hc_lean_m<decltype(hc)::value>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids,
-                                              w, logits, act, act_s, s_out, table, s);
-    });
-    if (err != hipSuccess) return err;
+    // stage 0: every launch; 1: router (+ shared gate/up); 2: the selection and
+    // the gate/up rows (one launch at M <= 4, two at M = 5..8); 3: the W2 launch
+    if (stage < 0 || stage > 3) return hipErrorInvalidValue;
+    if (stage <= 2) {
+        const hipError_t err = with_hc(H, [&](auto hc) {
+            return hc_lean_m<decltype(hc)::value>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm,
+                                                  ids, w, logits, act, act_s, s_out, table, stage,
+                                                  s);
+        });
+        if (err != hipSuccess || stage != 0) return err;
+    }
     return launch_w2(false, act, w2, ids, w, Is ? s_out : nullptr, M, H, I, K, table, y, s);
 }
 
@@ -1636,14 +1727,17 @@ static hipError_t launch_lean_m_t(const void *x, const void *wr, const void *w13
                                   const void *wsgu, const void *wsd, int M, int E, int I, int K,
                                   int Is, int renorm, int32_t *ids, float *w, float *logits,
                                   float *act, float *act_s, float *s_out, GroupTable *table,
-                                  hipStream_t s)
+                                  int stage, hipStream_t s)
 {
-    const int rb = (E + kWavesPerBlock - 1) / kWavesPerBlock;
-    hipLaunchKernelGGL((k_route_shared_m<HC, MT>), dim3(rb + Is / kWavesPerBlock), dim3(kBlock),
-                       0, s, (const f16 *)x, (const f16 *)wr, (const f16 *)wsgu, M, E, Is, logits,
-                       act_s);
-    hipError_t err = last();
-    if (err != hipSuccess) return err;
+    hipError_t err = hipSuccess;
+    if (stage != 2) {
+        const int rb = (E + kWavesPerBlock - 1) / kWavesPerBlock;
+        hipLaunchKernelGGL((k_route_shared_m<HC, MT>), dim3(rb + Is / kWavesPerBlock),
+                           dim3(kBlock), 0, s, (const f16 *)x, (const f16 *)wr,
+                           (const f16 *)wsgu, M, E, Is, logits, act_s);
+        err = last();
+        if (err != hipSuccess || stage == 1) return err;
+    }
     const int n_slots = M * K < E ? M * K : E;
     // without a shared expert the mapping is unused (no shared workgroups)
     const int lm_width = Is ? Is : 512;
@@ -1677,14 +1771,14 @@ template <int HC>
 hipError_t hc_lean_m(const void *x, const void *wr, const void *w13, const void *wsgu,
                      const void *wsd, int M, int E, int I, int K, int Is, int renorm,
                      int32_t *ids, float *w, float *logits, float *act, float *act_s,
-                     float *s_out, GroupTable *table, hipStream_t s)
+                     float *s_out, GroupTable *table, int stage, hipStream_t s)
 {
     switch (mt_of(M)) {
-    case 2: return launch_lean_m_t<HC, 2>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s);
-    case 4: return launch_lean_m_t<HC, 4>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s);
+    case 2: return launch_lean_m_t<HC, 2>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, stage, s);
+    case 4: return launch_lean_m_t<HC, 4>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, stage, s);
     case 8:
         if constexpr (HC <= 4)
-            return launch_lean_m_t<HC, 8>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, s);
+            return launch_lean_m_t<HC, 8>(x, wr, w13, wsgu, wsd, M, E, I, K, Is, renorm, ids, w, logits, act, act_s, s_out, table, stage, s);
         return hipErrorInvalidValue;
     }
     return hipErrorInvalidValue;
@@ -1699,7 +1793,7 @@ template hipError_t hc_lean<MOE_PART>(const void *, const void *, const void *, 
 template hipError_t hc_lean_m<MOE_PART>(const void *, const void *, const void *, const void *,
                                         const void *, int, int, int, int, int, int, int32_t *,
                                         float *, float *, float *, float *, float *, GroupTable *,
-                                        hipStream_t);
+                                        int, hipStream_t);
 
 #elif MOE_PART >= MOE_FIRST_LANE_PART && MOE_PART <= MOE_LAST_PART
 // ================================================================ parts 9..21: one lane mapping

@@ -301,7 +301,7 @@ def test_layer_stage_probe_validation():
                                      0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
 
     assert call(0) == -2 and call(7) == -2 and call(-1) == -2
-    assert call(2, M=2) == -2          # not the three-launch path
+    assert call(2, M=9) == -2          # stages 1..4 take the layer's sizes (M = 1..8)
     assert call(5, M=2) == -2          # not the single-launch path
     assert call(2, H=2000) == -2
     assert L.moe_dbg_layer_stage(2, None, FAKE, FAKE, FAKE, None, None, 1, 2048, 256, 512, 8, 0, 1,

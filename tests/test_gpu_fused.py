@@ -108,10 +108,14 @@ def test_fused_stack_graph_replays_match_eager():
     synth.SHAPES["full_e256_k8_i512"],                         # shared as wide as a routed expert
     synth.LayerShape(M=1, H=2048, E=64, K=8, I=512, Is=0),     # no shared expert
     synth.LayerShape(M=1, H=2048, E=64, K=8, I=512, Is=128),   # narrower shared expert
+    synth.SHAPES["batch2_e256_k8_i512"],                       # selection in the expand launch
+    synth.SHAPES["batch4_e256_k8_i512"],
+    synth.SHAPES["batch8_e256_k8_i512"],                       # a selection launch of its own
+    synth.LayerShape(M=3, H=1024, E=96, K=6, I=192, Is=0),     # odd sizes, no shared expert
 ], ids=_id)
 def test_layer_stages_in_order_equal_the_full_call(shape):
-    """The three launches run one at a time through moe_dbg_layer_stage (how
-    bench times each kernel) give the full call's outputs bit for bit."""
+    """The layer's three steps run one at a time through moe_dbg_layer_stage
+    (how bench times each step) give the full call's outputs bit for bit."""
     print("stages vs full call", shape, flush=True)
     t = cases.draw_case(shape, 5, DEV)
     full = DecodeLayer(t, shape)
@@ -155,3 +159,40 @@ def test_small_batch_stack_graph_replays_match_eager(name):
         if rep % 2 == 0:
             st.forward_eager()
             torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_tied_logits_shared_experts_layer_equals_separate_calls(M):
+    """Router rows in identical pairs (experts 2j and 2j+1 always tie) and
+    tokens that are small perturbations of one another, so the tokens share
+    most of their experts and break ties by id: the layer (which finds each
+    shared expert's tokens and slots from every token's own order) equals
+    the separate calls (which read them from the group table) bit for bit,
+    and every token's ids are the top-K of its own logits under (logit
+    descending, id ascending)."""
+    sh = synth.LayerShape(M=M, H=2048, E=128, K=8, I=256, Is=256)
+    print("tied pairs", sh, flush=True)
+    t = synth.draw_layer(sh, 21, DEV)
+    t["wr"] = t["wr"][0::2].repeat_interleave(2, dim=0).contiguous()
+    g = torch.Generator(device=DEV).manual_seed(77)
+    x0 = t["x"][:1].float()
+    noise = torch.randn((M, sh.H), generator=g, device=DEV) * 0.05
+    noise[0] = 0
+    t["x"] = (x0 + noise).half().contiguous()
+    a = DecodeLayer(t, sh, fused=False)
+    b = DecodeLayer(t, sh, fused=True)
+    a.forward()
+    b.forward()
+    torch.cuda.synchronize()
+    assert torch.equal(a.topk_ids, b.topk_ids)
+    assert torch.equal(a.topk_w, b.topk_w)
+    assert torch.equal(a.y, b.y)
+    lg = b.logits.cpu()
+    ids = b.topk_ids.cpu()
+    shared = 0
+    for m in range(M):
+        order = sorted(range(sh.E), key=lambda e: (-lg[m, e].item(), e))
+        assert ids[m].tolist() == order[:sh.K], m
+        if m:
+            shared += len(set(ids[m].tolist()) & set(ids[0].tolist()))
+    assert shared > 0  # the tokens do share experts

@@ -176,13 +176,19 @@ def test_w13_stage_matches_oracle():
         assert err < 1e-5, (k, e, err)
 
 
-def test_uniform_router_ties_to_lowest_ids():
-    sh = synth.LayerShape(M=2, H=2048, E=256, K=8, I=128, Is=0)
+@pytest.mark.parametrize("M", [2, 4, 8])
+def test_uniform_router_ties_to_lowest_ids(M):
+    # every logit 0: each token takes experts 0..K-1 in id order; the layer's
+    # token masks and slots (found from each token's order at M <= 4) place
+    # every activation where the separate calls' group table does
+    sh = synth.LayerShape(M=M, H=2048, E=256, K=8, I=128, Is=0)
     t = synth.draw_layer(sh, 1, DEV)
     t["wr"].zero_()
     layer = run_layer(t, sh)
-    assert layer.topk_ids.cpu().tolist() == [list(range(8))] * 2
+    assert layer.topk_ids.cpu().tolist() == [list(range(8))] * M
     assert torch.all(layer.topk_w == 0.125)
+    sep = run_layer(t, sh, fused=False)
+    assert torch.equal(layer.y, sep.y)
 
 
 def test_same_tokens_share_every_expert():
