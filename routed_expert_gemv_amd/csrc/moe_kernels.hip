@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
 // I] (or the shared expert's [M, Is]) staged in LDS once per workgroup of
 // kSWaves waves instead of every lane fetching its chunks of every (token,
 // slot) pair from L2 inside the combine loop.  The first batch of W2 rows is
-// requested before the staging loads, and every later batch before the
+// requested right after the staging loads, and every later batch before the
 // previous one is combined (experts still in order of first appearance).
 constexpr int kSWaves = 8;
 constexpr int kSBlock = kSWaves * kWave;
@@ -470,7 +470,12 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     constexpr int CPL = LM::CPL;
     constexpr int RPL = kWave / LPR;
     const int nch = I / 8;
-    constexpr int BATCH = 8 / CPL; // 16-byte W2 chunks per lane per buffer: 8
+    // experts per buffer: 2 at CPL = 1, else 1 (2 or more 16-byte chunks per
+    // lane).  Two buffers keep at most 4 experts' rows in flight per wave: in
+    // one process with the replays interleaved, batches of 2 / 4 / 8 experts
+    // give M = 8 70.3 / 72.1 / 73.5, M = 4 39.8 / 40.1 / 41.7 us per layer
+    // (1 expert: 74.2 and 41.5), so fewer experts read at once stream faster.
+    constexpr int BATCH = CPL == 1 ? 2 : 1;
     const int lane = lane_id();
     const int wave = threadIdx.x / kWave;
     const int r = lane / LPR;
@@ -535,6 +540,22 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
         const int q = threadIdx.x + i * kSBlock;
         st0[i] = a4[q < n4 ? q : n4 - 1];
     }
+    // the rest of act (K*I > 4096): 16-byte chunks, 4 in flight per thread
+    // per step, staged before the first batch is requested (so that no load
+    // of this loop is still outstanding once the batches are)
+    for (int q0 = kSReg * kSBlock; q0 < n4; q0 += 4 * kSBlock) {
+        f32x4 st[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = q0 + threadIdx.x + i * kSBlock;
+            st[i] = a4[q < n4 ? q : n4 - 1];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = q0 + threadIdx.x + i * kSBlock;
+            if (q < n4) l4[q] = st[i];
+        }
+    }
     // keep the batch's loads together, after the staging loads and ahead of
     // the LDS stores (which wait)
     __builtin_amdgcn_sched_barrier(0);
@@ -553,20 +574,6 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     for (int i = 0; i < kSReg; ++i) {
         const int q = threadIdx.x + i * kSBlock;
         l4[q < n4 ? q : n4 - 1] = st0[i];
-    }
-    // the rest of act (K*I > 4096): 16-byte chunks, 4 in flight per thread per step
-    for (int q0 = kSReg * kSBlock; q0 < n4; q0 += 4 * kSBlock) {
-        f32x4 st[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = q0 + threadIdx.x + i * kSBlock;
-            st[i] = a4[q < n4 ? q : n4 - 1];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = q0 + threadIdx.x + i * kSBlock;
-            if (q < n4) l4[q] = st[i];
-        }
     }
     __syncthreads();
 
