@@ -135,6 +135,8 @@ def test_staged_down_kernel_at_64k_lds():
     synth.LayerShape(M=7, H=512, E=16, K=3, I=64, Is=64),
     synth.LayerShape(M=1, H=2048, E=16, K=1, I=128, Is=128),          # K = 1: dense SwiGLU
     synth.LayerShape(M=2, H=2048, E=16, K=16, I=128, Is=0),           # K = E: every expert
+    synth.LayerShape(M=2, H=2048, E=16, K=1, I=128, Is=128),          # K = 1 at M > 1
+    synth.LayerShape(M=4, H=1024, E=8, K=8, I=64, Is=64),             # K = E at M = 4
     synth.LayerShape(M=8, H=512, E=1024, K=16, I=64, Is=0),           # largest E, K, M
     synth.LayerShape(M=2, H=2048, E=8, K=2, I=2048, Is=2048),         # largest I
     synth.LayerShape(M=4, H=4096, E=16, K=4, I=1024, Is=512),         # largest H
