@@ -172,9 +172,11 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
  * first launch and its down rows in the second.  For
  * M = 2..8: the router and shared gate/up rows; the distinct experts' gate/up
  * rows with the shared down rows; the down rows with the combine -- three
- * launches for M <= 4, where each workgroup of the second launch selects
- * every token's experts and groups the distinct ones itself, four for
- * M = 5..8, where one workgroup does that in a launch of its own.
+ * launches for M <= 4, where the workgroups of the second launch select
+ * themselves (those of token 0's experts with only as many top-k rounds as
+ * they need, the others every token's selection and the grouping of the
+ * distinct experts), four for M = 5..8, where one workgroup selects and
+ * groups in a launch of its own.
  * Other sizes run the three calls' kernels in sequence.  See
  * moe_layer_launches.
  *   x, w_router, w13, w2  as for moe_route / moe_decode_fused
