@@ -28,6 +28,24 @@ def test_stage_bytes_cover_the_layer_once():
         assert st["k_reduce"] >= 2 * sh.K * sh.H * sh.I + 2 * sh.H * sh.Is
 
 
+def test_small_batch_step_bytes_cover_the_layer_once():
+    # the three steps of an M-token layer read the router, each distinct
+    # expert's W13 and W2 and the shared expert once, plus small hand-off
+    # tensors (logits, routing outputs, activations, shared output, x, y)
+    for name in ("batch2_e256_k8_i512", "batch4_e256_k8_i512", "batch8_e256_k8_i512"):
+        sh = synth.SHAPES[name]
+        for nd in (sh.K, 16.5, min(sh.M * sh.K, sh.E)):
+            st = bench.stage_bytes_m(sh, nd)
+            assert list(st) == list(bench.STAGES_M if sh.M <= 4 else bench.STAGES_M8)
+            expert, total = bench.layer_bytes(sh, nd)
+            extra = sum(st.values()) - total
+            assert 0 <= extra < 0.03 * total, (name, nd, extra, total)
+            route, expand, w2 = st.values()
+            assert route >= 2 * sh.E * sh.H + 2 * 2 * sh.Is * sh.H
+            assert expand >= 2 * 2 * nd * sh.I * sh.H + 2 * sh.H * sh.Is
+            assert w2 >= 2 * nd * sh.H * sh.I
+
+
 def test_committed_counters_use_the_same_accounting():
     c = json.load(open(bench.COUNTERS))
     st = bench.stage_bytes(synth.SHAPES["full_e256_k8_i512"])
