@@ -20,7 +20,8 @@ Reported (one JSON line): expert-byte throughput in GB/s (value), us/layer,
 fraction of the 8 TB/s HBM peak, the roofline of the dominant kernel (the
 expand kernel, timed with HIP events over graphs of that kernel alone, next to
 the average of the same graphs in the committed rocprofv3 trace when it was
-taken on the current sources) and the fp64 oracle timed on this host's cores
+taken on the current sources; with --tokens, the dominant step of the layer's
+three, timed the same way) and the fp64 oracle timed on this host's cores
 (one core and all of them) on a bounded sample of the same layers.
 
 With --prefill T the workload is the many-token layer instead: a stack of
