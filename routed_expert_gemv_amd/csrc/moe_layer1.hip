@@ -15,8 +15,9 @@
 //     waits give up (below), which changes the speed and not the results;
 //   * router: each XCD computes all E logits itself (its 32 workgroups, one
 //     row per wave) and hands them over through its own L2: plain stores, a
-//     per-workgroup flag, sc1 (device-coherent) polls.  No atomics anywhere:
-//     every workgroup keeps its own call counter (epoch) in the workspace, all
+//     per-workgroup flag, sc1 (device-coherent) polls.  No atomics in the
+//     hand-offs (only a wait that gives up counts itself with one): every
+//     workgroup keeps its own call counter (epoch) in the workspace, all
 //     counters advance in lockstep, and a flag is current when it holds this
 //     call's epoch;
 //   * each workgroup then selects the experts itself (only as many top-k
