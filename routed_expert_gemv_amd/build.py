@@ -23,8 +23,12 @@ HEADERS = [os.path.join(CSRC, "moe_internal.h"), os.path.join(CSRC, "moe_device.
            os.path.join(INCLUDE, "moe_decode.h"), os.path.join(INCLUDE, "moe_prefill.h")]
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for every HIP file of this library.
+# Kernel arguments are preloaded into SGPRs at dispatch (up to 16 dwords; the
+# compiler keeps a loader in front of each kernel for firmware that does not
+# preload): a kernel's first loads then need not wait for its arguments.
 HIPCC_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
-               "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+               "-Wall", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def hipcc() -> str:
@@ -34,8 +38,10 @@ def hipcc() -> str:
 
 
 def source_id() -> str:
-    """SHA-256 (hex) over the names and contents of the sources and headers."""
+    """SHA-256 (hex) over the compiler flags and the names and contents of the
+    sources and headers."""
     h = hashlib.sha256()
+    h.update(" ".join(HIPCC_FLAGS).encode() + b"\0")
     for path in sorted(SOURCES + HEADERS):
         h.update(os.path.basename(path).encode() + b"\0")
         with open(path, "rb") as fh:
