@@ -23,6 +23,24 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kLoadNT = 2;
 
 // ---------------------------------------------------------------- helpers
+// Staging order of a buffer of n4 16-byte chunks that every workgroup copies
+// into its LDS (the activations): chunk q of the loop is chunk
+// staged_chunk(q, n4, rot), the order rotated by a start that depends on the
+// workgroup's place among those of its XCD (workgroups are dealt to the 8
+// XCDs in turn), so that the 32 workgroups of an XCD, which copy the same
+// bytes at the same time, do not request the same L2 lines at once.  Indices
+// past the end map to the last chunk of the unrotated order, whose copy
+// stores its own value again.
+__device__ __forceinline__ int stage_rotation(int n4)
+{
+    return (int)(((blockIdx.x >> 3) & 31u) * (unsigned)(n4 >> 5));
+}
+__device__ __forceinline__ int staged_chunk(int q, int n4, int rot)
+{
+    const int x = (q < n4 ? q : n4 - 1) + rot;
+    return x >= n4 ? x - n4 : x;
+}
+
 __device__ __forceinline__ f16x8 stream_load(const f16x8 *p)
 {
     return __builtin_nontemporal_load(p);
