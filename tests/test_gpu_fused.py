@@ -36,6 +36,10 @@ SHAPES = [
     synth.LayerShape(M=2, H=4096, E=64, K=4, I=256, Is=256),
     synth.LayerShape(M=8, H=1024, E=32, K=4, I=128, Is=0),
     synth.LayerShape(M=3, H=2048, E=1024, K=16, I=64, Is=64),
+    # the selection launch with 4, 16 and 1 logits per lane
+    synth.LayerShape(M=6, H=2048, E=256, K=8, I=256, Is=256),
+    synth.LayerShape(M=7, H=1024, E=1024, K=16, I=64, Is=64),
+    synth.LayerShape(M=5, H=512, E=64, K=6, I=128, Is=0, renormalize=False),
     # the same entry point runs the separate kernels
     synth.LayerShape(M=1, H=2048, E=16, K=16, I=2048, Is=0),        # K*I above the LDS stage
 ] + cases.WIDE_SHAPES
