@@ -41,6 +41,24 @@ __device__ __forceinline__ int staged_chunk(int q, int n4, int rot)
     return x >= n4 ? x - n4 : x;
 }
 
+// Element h of rows 0..MT-1 of an [M, H] fp32 tensor (the shared-expert
+// output that the W2 kernels add after their combine), 0 for rows past M or
+// for a null tensor.  The W2 kernels request it before their weight stream:
+// a load after the combine would cost every wave a full memory latency per
+// token at its end.  The loads go through a buffer range that is empty for a
+// null tensor and ends at row M, so every load is issued unconditionally and
+// none touches memory outside the tensor.
+template <int MT>
+__device__ __forceinline__ void load_column(const float *t, int M, int H, int h, float (&v)[MT])
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(t), (short)0, t ? M * H * (int)sizeof(float) : 0, kBufferWord3);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        v[m] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(m * H + h) * 4u, 0, 0));
+}
+
 __device__ __forceinline__ f16x8 stream_load(const f16x8 *p)
 {
     return __builtin_nontemporal_load(p);

@@ -383,6 +383,8 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
     const int r = lane / LPR;
     const int cl = lane % LPR;
     const int h = (blockIdx.x * kWavesPerBlock + wave) * RPL + r;
+    float s_row[MT];
+    load_column<MT>(SHARED ? nullptr : shared_in, M, H, h, s_row);
 
     const int n_u = SHARED ? 1 : (MT == 1 ? K : table->n_u);
     float acc[MT];
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
             if (SHARED) {
                 static_cast<float *>(out)[o] = t;
             } else {
-                const float v = shared_in ? t + shared_in[o] : t;
+                const float v = shared_in ? t + s_row[m] : t;
                 static_cast<f16 *>(out)[o] = (f16)v;
             }
         }
@@ -482,6 +484,8 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
     const int cl = lane % LPR;
     const int h = (blockIdx.x * kSWaves + wave) * RPL + r;
     const int slots = SHARED ? 1 : K;
+    float s_row[MT];
+    load_column<MT>(SHARED ? nullptr : shared_in, M, H, h, s_row);
     const int n_u = SHARED ? 1 : table->n_u;
 
     // two batches of W2 rows: the next batch is requested before the current
@@ -618,7 +622,7 @@ __global__ __launch_bounds__(kSBlock) void k_w2_staged(
             if (SHARED) {
                 static_cast<float *>(out)[o] = t;
             } else {
-                const float v = shared_in ? t + shared_in[o] : t;
+                const float v = shared_in ? t + s_row[m] : t;
                 static_cast<f16 *>(out)[o] = (f16)v;
             }
         }
