@@ -1169,9 +1169,16 @@ __global__ __launch_bounds__(kBlock) void k_expand_m(const f16 *__restrict__ x,
 // build the group table in LDS (the same device functions as k_select_m)
 // before they request their rows.  Workgroup 0 (entry 0) also runs the full
 // selection while its rows are in flight and, after its products, writes
-// ids, weights and the table that the W2 kernel reads.  The shared
-// workgroups are k_expand_m's.  (At M = 8 each wave would select for two
-// tokens in turn, and the selection launch is kept.)
+// ids, weights and the table that the W2 kernel reads.  After their rows, token
+// 0's workgroups (which start first) also compute the shared down rows, the
+// work of k_expand_m's shared workgroups with the same arithmetic.  As
+// separate workgroups at the end of the grid they ran in a later round of
+// resident workgroups and lengthened the launch: M = 2 23.89 -> 23.74 and
+// M = 4 38.59 -> 38.37 us per layer with them folded in (replays
+// interleaved).  First in the grid they delayed token 0's experts (M = 4
+// 38.60 -> 38.77 us), and between those and the later entries too (M = 2
+// 23.94 -> 24.34 us).  (At M = 8 each wave would select for two tokens in
+// turn, and the selection launch is kept.)
 template <int HC, int MT, class LM, int NPL>
 __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
     const f16 *__restrict__ x, const f16 *__restrict__ w13, const f16 *__restrict__ wsd,
@@ -1187,18 +1194,9 @@ __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
     __shared__ int32_t sids[kMaxSlots];
     __shared__ int s_e;
     __shared__ int s_rank[MT];
-    // (the shared down workgroups last here: first in the grid, M = 4 measured
-    // 38.60 -> 38.77 us per layer, the routed workgroups of token 0's experts
-    // then starting later; between those and the later entries, M = 2 23.94 ->
-    // 24.34 and M = 4 38.67 -> 38.88 us)
     const int b = blockIdx.x;
     const int lane = lane_id();
-    if (b >= routed_blocks) {
-        shared_down_block<LM, MT, MT * HC * kWave>(wsd, act_s, M, H, Is,
-                                                   (b - routed_blocks) * kWavesPerBlock, s_out,
-                                                   reinterpret_cast<f32x4 *>(xs));
-        return;
-    }
+    (void)routed_blocks; // every workgroup is a routed one
     const int wave = threadIdx.x / kWave;
     constexpr int kRowsPerBlockM = rows_per_wave_m<false, MT>() * kWavesPerBlock;
     const int u = b / (I / kRowsPerBlockM);
@@ -1277,6 +1275,17 @@ __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
         int *dst = reinterpret_cast<int *>(table);
         for (int i = threadIdx.x; i < (int)(sizeof(GroupTable) / sizeof(int)); i += kBlock)
             dst[i] = src[i];
+    }
+    // then the shared down rows: token 0's workgroups take the shared down
+    // blocks sb = b, b + (their count), ...
+    if (Is > 0) {
+        const int r0 = K * (I / kRowsPerBlockM);
+        const int shared_blocks = H / (kWavesPerBlock * (kWave / LM::LPR));
+        for (int sb = b; sb < shared_blocks; sb += r0) {
+            __syncthreads(); // xs is free again
+            shared_down_block<LM, MT, MT * HC * kWave>(wsd, act_s, M, H, Is, sb * kWavesPerBlock,
+                                                       s_out, reinterpret_cast<f32x4 *>(xs));
+        }
     }
 }
 
@@ -1833,8 +1842,7 @@ static hipError_t launch_lean_m_t(const void *x, const void *wr, const void *w13
         const int routed = n_slots * (I / (rows_per_wave_m<false, MT>() * kWavesPerBlock));
         return with_lane_map(lm_width, [&](auto lm) {
             using LM = decltype(lm);
-            const int shared = Is ? H / (kWavesPerBlock * (kWave / LM::LPR)) : 0;
-            const dim3 grid(routed + shared);
+            const dim3 grid(routed); // the shared down rows go with token 0's workgroups
 #define SEL_LAUNCH(NPL_)                                                                          \
     hipLaunchKernelGGL((k_expand_sel_m<HC, MT, LM, NPL_>), grid, dim3(kBlock), 0, s,              \
                        (const f16 *)x, (const f16 *)w13, (const f16 *)wsd, act_s, logits, M, H, E, \
