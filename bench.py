@@ -654,9 +654,23 @@ def summarize_trace(trace_dir, out_path, cmd, bench_line=None):
     print("\n".join(lines))
 
 
+# Launch structures whose floor probes() measures: the bytes each launch of a
+# full-width layer reads (router rows; gate/up rows with the shared ones; down
+# rows with the shared ones), and the same bytes with the down rows moved into
+# the gate/up launch (split-K partial sums), with and without a launch that
+# sums the partials.
+FLOOR_STRUCTURES = {
+    "router+expand+reduce": (1053696, 37772352, 18896960),
+    "router+expand_with_down+partial_sum": (1053696, 37772352 + 18896960, 1048576),
+    "router+expand_with_down": (1053696, 37772352 + 18896960),
+}
+
+
 def probes(dev):
-    """Empty-kernel launch latency, hipGraph kernel-node gap, and the read
-    bandwidth of a 2 GiB stream (the practical HBM ceiling)."""
+    """Empty-kernel launch latency, hipGraph kernel-node gap, the read
+    bandwidth of a 2 GiB stream (the practical HBM ceiling), and the floor per
+    layer of the launch structures above: pure streams of each launch's bytes,
+    36 layers on distinct buffers in one graph."""
     import torch
     import routed_expert_gemv_amd as moe
 
@@ -703,7 +717,31 @@ def probes(dev):
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / 10
     res["read_2GiB_GBs"] = round(buf.numel() * 2 / (ms * 1e-3) / 1e9, 1)
-    del buf
+
+    flat = buf.view(torch.uint8)
+    floors = {}
+    for name, sizes in FLOOR_STRUCTURES.items():
+        padded = [(n + 4095) // 4096 * 4096 for n in sizes]
+        stride = sum(padded)
+        assert stride * LAYERS <= flat.numel()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for layer in range(LAYERS):
+                off = layer * stride
+                for n, p in zip(sizes, padded):
+                    moe.moe_probe_read(flat[off:off + n], out)
+                    off += p
+        g.replay()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(10):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        floors[name] = round(a.elapsed_time(b) * 1e3 / (10 * LAYERS), 3)
+        del g
+    res["layer_floor_us"] = floors
+    del flat, buf
     torch.cuda.empty_cache()
     return res
 

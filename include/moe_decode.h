@@ -262,9 +262,11 @@ moe_status moe_dbg_layer_stage(int stage, const void *x, const void *w_router, c
 moe_status moe_probe_empty(hipStream_t stream);
 
 /* Streams `bytes` (a multiple of 16) of device memory at `src` with
- * non-temporal 16-byte loads (8 in flight per thread): the achievable read
- * bandwidth.  out: one device float, written only in a case that zero-filled
- * input never produces. */
+ * non-temporal 16-byte loads (8 in flight per thread; 1 per thread below
+ * 4 MiB, so that short reads still spread over many workgroups): the
+ * achievable read bandwidth, and the floor of a launch structure timed with
+ * several reads in a graph.  out: one device float, written only in a case
+ * that zero-filled input never produces. */
 moe_status moe_probe_read(const void *src, size_t bytes, float *out, hipStream_t stream);
 
 /* Copies `bytes` (a multiple of 16) from src to dst (device, not overlapping)

@@ -1294,11 +1294,11 @@ __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
 // empty kernel (launch latency and graph node gap)
 __global__ void k_probe_empty() {}
 
-// stream `n16` 16-byte chunks with non-temporal loads, 8 per thread in flight
+// stream `n16` 16-byte chunks with non-temporal loads, L per thread in flight
+template <int L>
 __global__ __launch_bounds__(256) void k_probe_read(const f16x8 *__restrict__ src, size_t n16,
                                                     float *__restrict__ out)
 {
-    constexpr int L = 8;
     const size_t base = (size_t)blockIdx.x * blockDim.x * L + threadIdx.x;
     f16x8 v[L];
 #pragma unroll
@@ -1591,10 +1591,20 @@ hipError_t launch_probe_empty(hipStream_t s)
 
 hipError_t launch_probe_read(const void *src, size_t bytes, float *out, hipStream_t s)
 {
+    // below 4 MB one load per thread, so that a short read still spreads over
+    // hundreds of workgroups (a layer's router-sized read: 257 of them)
     const size_t n16 = bytes / 16;
-    const size_t per_block = 256 * 8;
-    const unsigned blocks = (unsigned)((n16 + per_block - 1) / per_block);
-    hipLaunchKernelGGL(k_probe_read, dim3(blocks), dim3(256), 0, s, (const f16x8 *)src, n16, out);
+    if (n16 == 0) return hipSuccess;
+    if (bytes < (4u << 20)) {
+        const unsigned blocks = (unsigned)((n16 + 255) / 256);
+        hipLaunchKernelGGL(k_probe_read<1>, dim3(blocks), dim3(256), 0, s, (const f16x8 *)src,
+                           n16, out);
+    } else {
+        const size_t per_block = 256 * 8;
+        const unsigned blocks = (unsigned)((n16 + per_block - 1) / per_block);
+        hipLaunchKernelGGL(k_probe_read<8>, dim3(blocks), dim3(256), 0, s, (const f16x8 *)src,
+                           n16, out);
+    }
     return last();
 }
 
