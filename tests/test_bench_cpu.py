@@ -110,3 +110,22 @@ def test_pmc_summary_derives_memory_unit_busy(tmp_path):
     # TA busy 200 cycles on average over one XCD's 1000 cycles
     assert line.rstrip(" |").endswith("20.0")
     assert "at::native" not in out.read_text()
+
+
+def test_floor_probe_streams_the_layer_bytes():
+    """The launch-structure floors that bench.py's probes measure read the
+    full-width layer's bytes launch by launch: the router, expand and reduce
+    launches' algorithmic bytes, and the same bytes with the down rows moved
+    into the gate/up launch (plus a 1 MiB partial-sum read where a third
+    launch remains)."""
+    st = bench.stage_bytes(synth.SHAPES["full_e256_k8_i512"])
+    router, expand, reduce = st["k_router1"], st["k_expand"], st["k_reduce"]
+    fs = bench.FLOOR_STRUCTURES
+    assert fs["router+expand+reduce"] == (router, expand, reduce)
+    assert fs["router+expand_with_down"] == (router, expand + reduce)
+    assert fs["router+expand_with_down+partial_sum"][:2] == (router, expand + reduce)
+    assert fs["router+expand_with_down+partial_sum"][2] == 1 << 20
+    for sizes in fs.values():
+        assert all(n % 16 == 0 for n in sizes)
+        # 36 layers on distinct 4 KiB-aligned buffers fit the 2 GiB probe buffer
+        assert bench.LAYERS * sum((n + 4095) // 4096 * 4096 for n in sizes) <= 2 << 30
