@@ -175,8 +175,10 @@ moe_status moe_decode_fused(const void *x, const void *w13, const void *w2,
  * launches for M <= 4, where the workgroups of the second launch select
  * themselves (those of token 0's experts with only as many top-k rounds as
  * they need, the others every token's selection and the grouping of the
- * distinct experts), four for M = 5..8, where one workgroup selects and
- * groups in a launch of its own.
+ * distinct experts; token 0's workgroups also compute the shared down rows,
+ * unless those outnumber what they take, which then get a launch of their
+ * own first), four for M = 5..8, where one workgroup selects and groups in a
+ * launch of its own.
  * Other sizes run the three calls' kernels in sequence.  See
  * moe_layer_launches.
  *   x, w_router, w13, w2  as for moe_route / moe_decode_fused
@@ -210,8 +212,12 @@ moe_status moe_layer_decode_noalloc(const void *x, const void *w_router, const v
                                     int32_t *topk_ids, float *topk_w, float *logits, void *y,
                                     hipStream_t stream);
 
-/* Number of kernels moe_layer_decode enqueues for these sizes (3 at M = 1..4,
- * 4 at M = 5..8), 0 for unsupported sizes or M = 0. */
+/* Number of kernels moe_layer_decode enqueues for these sizes: 3 at
+ * M = 1..4 (4 at M = 2..4 when the shared expert's down rows outnumber what
+ * token 0's gate/up workgroups take, for example K = 1 with narrow experts
+ * and a wide shared expert, and they get a launch of their own), 4 at
+ * M = 5..8; more where it runs the three calls' kernels; 0 for unsupported
+ * sizes or M = 0. */
 int moe_layer_launches(int M, int H, int E, int I, int K, int Is);
 
 /* ---- test-only probes (not part of the decode path) --------------------- */
@@ -224,7 +230,8 @@ int moe_layer_launches(int M, int H, int E, int I, int K, int Is);
  * (Is != I)), 3 = reduce (reads those; writes y).  At M = 2..8: 1 = router and
  * shared gate/up rows (logits, shared activations), 2 = the selection and the
  * distinct experts' gate/up rows with the shared down rows (one launch at
- * M <= 4, two at M = 5..8; topk_ids, topk_w, the group table, the routed
+ * M <= 4 (two where the shared down rows get a launch of their own), two at
+ * M = 5..8; topk_ids, topk_w, the group table, the routed
  * activations, the shared output), 3 = the down rows and the combine (y).  A
  * stage reads what the previous stage left in the same buffers, so only a
  * full call (or stages 1, 2, 3 in order) on them makes its inputs valid.

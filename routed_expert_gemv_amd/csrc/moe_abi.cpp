@@ -251,7 +251,7 @@ int moe_layer_launches(int M, int H, int E, int I, int K, int Is)
     if (lean_ok(M, H, E, I, K, Is)) return 3;
     // M <= 4: router, expand with the selection folded in, W2; else a
     // separate selection launch before the expand
-    if (lean_m_ok(M, H, E, I, K, Is)) return mt_of(M) <= 4 ? 3 : 4;
+    if (lean_m_ok(M, H, E, I, K, Is)) return lean_m_launches(M, H, I, K, Is);
     // shared_expert (2) + moe_route (2) + moe_decode_fused (2)
     return (Is ? 2 : 0) + 2 + 2;
 }

@@ -115,6 +115,9 @@ void lane_map_of(int n, int *lpr, int *cpl, int *pad);
 // launch at M = 5..8); the staged W2 kernel.  stage 0 runs every launch,
 // stage 1..3 one of those three steps alone.
 bool lean_m_ok(int M, int H, int E, int I, int K, int Is);
+// kernels launch_lean_m enqueues for these sizes (3, or 4 with a selection
+// launch at M = 5..8 or a shared down launch of its own at M <= 4)
+int lean_m_launches(int M, int H, int I, int K, int Is);
 hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const void *w2,
                          const void *wsgu, const void *wsd, int M, int H, int E, int I, int K,
                          int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,

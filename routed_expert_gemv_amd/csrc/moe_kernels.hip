@@ -459,6 +459,9 @@ __global__ __launch_bounds__(kBlock) void k_w2_combine(
 // requested right after the staging loads, and every later batch before the
 // previous one is combined (experts still in order of first appearance).
 constexpr int kSWaves = 8;
+// shared down blocks that each of token 0's workgroups takes in the M <= 4
+// expand launch at most (the benched sizes: 1 at M = 2, 2 at M = 4)
+constexpr int kSharedPerTok0 = 4;
 constexpr int kSBlock = kSWaves * kWave;
 
 template <class LM, int MT, bool SHARED>
@@ -1171,7 +1174,9 @@ __global__ __launch_bounds__(kBlock) void k_expand_m(const f16 *__restrict__ x,
 // selection while its rows are in flight and, after its products, writes
 // ids, weights and the table that the W2 kernel reads.  After their rows, token
 // 0's workgroups (which start first) also compute the shared down rows, the
-// work of k_expand_m's shared workgroups with the same arithmetic.  As
+// work of k_expand_m's shared workgroups with the same arithmetic, up to
+// kSharedPerTok0 blocks each (beyond that, those workgroups run on their own
+// in a launch of k_expand_m before this one).  As
 // separate workgroups at the end of the grid they ran in a later round of
 // resident workgroups and lengthened the launch: M = 2 23.89 -> 23.74 and
 // M = 4 38.59 -> 38.37 us per layer with them folded in (replays
@@ -1277,14 +1282,18 @@ __global__ __launch_bounds__(kBlock) void k_expand_sel_m(
             dst[i] = src[i];
     }
     // then the shared down rows: token 0's workgroups take the shared down
-    // blocks sb = b, b + (their count), ...
+    // blocks sb = b, b + (their count), ... -- at most kSharedPerTok0 each;
+    // with more, the blocks run on their own in a launch before this one
     if (Is > 0) {
         const int r0 = K * (I / kRowsPerBlockM);
         const int shared_blocks = H / (kWavesPerBlock * (kWave / LM::LPR));
-        for (int sb = b; sb < shared_blocks; sb += r0) {
-            __syncthreads(); // xs is free again
-            shared_down_block<LM, MT, MT * HC * kWave>(wsd, act_s, M, H, Is, sb * kWavesPerBlock,
-                                                       s_out, reinterpret_cast<f32x4 *>(xs));
+        if (shared_blocks <= kSharedPerTok0 * r0) {
+            for (int sb = b; sb < shared_blocks; sb += r0) {
+                __syncthreads(); // xs is free again
+                shared_down_block<LM, MT, MT * HC * kWave>(wsd, act_s, M, H, Is,
+                                                           sb * kWavesPerBlock, s_out,
+                                                           reinterpret_cast<f32x4 *>(xs));
+            }
         }
     }
 }
@@ -1655,6 +1664,16 @@ bool lean_m_ok(int M, int H, int E, int I, int K, int Is)
     return M >= 2 && M <= kMaxTokens && (Is == 0 || H % (kWavesPerBlock * (kWave / lpr_of(Is))) == 0);
 }
 
+int lean_m_launches(int M, int H, int I, int K, int Is)
+{
+    if (mt_of(M) > kWavesPerBlock) return 4; // a selection launch
+    const int rows = (mt_of(M) == 4 ? rows_per_wave_m<false, 4>() : rows_per_wave_m<false, 2>()) *
+                     kWavesPerBlock;
+    const int r0 = K * (I / rows);
+    const int shared = Is ? H / (kWavesPerBlock * (kWave / lpr_of(Is))) : 0;
+    return shared > kSharedPerTok0 * r0 ? 4 : 3;
+}
+
 hipError_t launch_lean_m(const void *x, const void *wr, const void *w13, const void *w2,
                          const void *wsgu, const void *wsd, int M, int H, int E, int I, int K,
                          int Is, int renorm, int32_t *ids, float *w, float *logits, void *y,
@@ -1852,7 +1871,20 @@ static hipError_t launch_lean_m_t(const void *x, const void *wr, const void *w13
         const int routed = n_slots * (I / (rows_per_wave_m<false, MT>() * kWavesPerBlock));
         return with_lane_map(lm_width, [&](auto lm) {
             using LM = decltype(lm);
-            const dim3 grid(routed); // the shared down rows go with token 0's workgroups
+            // the shared down blocks go with token 0's K*I/rows workgroups,
+            // up to kSharedPerTok0 each; beyond that they run first, on their
+            // own, as k_expand_m's shared workgroups (one more launch, for
+            // sizes such as K = 1 with narrow experts and a wide shared one)
+            const int shared = Is ? H / (kWavesPerBlock * (kWave / LM::LPR)) : 0;
+            const int r0 = K * (I / (rows_per_wave_m<false, MT>() * kWavesPerBlock));
+            if (shared > kSharedPerTok0 * r0) {
+                hipLaunchKernelGGL((k_expand_m<HC, MT, LM>), dim3(shared), dim3(kBlock), 0, s,
+                                   (const f16 *)x, (const f16 *)w13, (const f16 *)wsd, act_s, M,
+                                   H, I, K, Is, 0, act, s_out, table);
+                const hipError_t e = last();
+                if (e != hipSuccess) return e;
+            }
+            const dim3 grid(routed);
 #define SEL_LAUNCH(NPL_)                                                                          \
     hipLaunchKernelGGL((k_expand_sel_m<HC, MT, LM, NPL_>), grid, dim3(kBlock), 0, s,              \
                        (const f16 *)x, (const f16 *)w13, (const f16 *)wsd, act_s, logits, M, H, E, \

@@ -286,6 +286,11 @@ def test_layer_launch_counts():
     assert L.moe_layer_launches(1, 2048, 256, 512, 8, 0) == 3
     assert L.moe_layer_launches(2, 2048, 256, 512, 8, 512) == 3    # up to 4 tokens: selection folded
     assert L.moe_layer_launches(4, 2048, 256, 512, 8, 512) == 3
+    # K = 1 with narrow experts and a wide shared one: more shared down
+    # blocks than token 0's workgroups take, so they get a launch of their own
+    assert L.moe_layer_launches(2, 4096, 64, 64, 1, 2048) == 4
+    assert L.moe_layer_launches(2, 2048, 16, 128, 1, 128) == 4     # 128 shared blocks, 16 of token 0
+    assert L.moe_layer_launches(2, 2048, 16, 128, 4, 128) == 3     # 128 shared blocks, 64 of token 0
     assert L.moe_layer_launches(5, 2048, 256, 512, 8, 512) == 4    # 5..8 tokens: a selection launch
     assert L.moe_layer_launches(8, 2048, 256, 512, 8, 512) == 4
     assert L.moe_layer_launches(1, 2048, 16, 2048, 16, 0) == 4     # K*I above the LDS stage

@@ -58,7 +58,10 @@ def test_layer_decode_against_separate_calls(shape):
     a.forward()
     launches = moe.moe_layer_launches(shape.M, shape.H, shape.E, shape.I, shape.K, shape.Is)
     if shape.M > 1:
-        assert launches == (3 if shape.M <= 4 else 4)
+        # 3; 4 with the selection launch (M = 5..8) or with a shared down
+        # launch of its own (M <= 4, when token 0's workgroups are too few
+        # for the shared down blocks)
+        assert launches in ((3, 4) if shape.M <= 4 else (4,))
     else:
         assert launches == (3 if shape.K * shape.I <= 16384 else 4 + (2 if shape.Is else 0))
     first = None
