@@ -1,4 +1,4 @@
-"""48 seeded random layer sizes across the accepted range (CPU-drawn sizes,
+"""96 seeded random layer sizes across the accepted range (CPU-drawn sizes,
 fixed seed, so the list is the same in every run): for each, moe_layer_decode
 against the three entry points bit for bit (routing outputs and y), the
 layer's steps run one at a time against the full call bit for bit, and the
@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _shapes(n=48, seed=20261203):
+def _shapes(n=96, seed=20261203):
     rng = random.Random(seed)
     out = []
     while len(out) < n:
